@@ -1,0 +1,58 @@
+"""Test-side glue: run the oracle on a generated problem, compare results."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+
+def oracle_output(problem, requests=None) -> np.ndarray:
+    """fp64 oracle output [B'][R][Hq][D] for a ``skvgen.Problem``."""
+    s = problem.spec
+    return oracle.decode_attention(
+        problem.host_arrays(), R=s.R, Hq=s.Hq, Hkv=s.Hkv, D=s.D, causal=s.causal,
+        window=s.window, scale=s.scale, q_dtype=s.q_dtype, kv_dtype=s.kv_dtype,
+        paged=problem.paged, block_size=s.block_size, v_layout=s.v_layout,
+        has_sink=s.sinks, requests=requests)
+
+
+def compare(out: np.ndarray, ref: np.ndarray, kind: str) -> dict:
+    """Error statistics of ``out`` vs the fp64 ``ref`` (same shape, last dim = D).
+
+    kind "f32": max-abs <= 2e-3 and max-rel <= 2e-3 over |ref| >= 2e-3, rel-L2 <= 1e-4.
+    kind "lowp": |out - ref| <= 5e-3 + 5e-3 |ref| elementwise, rel-L2 <= 1e-2 and
+    min row cosine >= 0.9999 over rows with a nonzero reference.
+    """
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    d = np.abs(out - ref)
+    nrm = np.linalg.norm(ref)
+    rel_l2 = float(np.linalg.norm(out - ref) / nrm) if nrm > 0 else float(np.linalg.norm(out))
+    o2 = out.reshape(-1, out.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    rn = np.linalg.norm(r2, axis=1)
+    on = np.linalg.norm(o2, axis=1)
+    live = rn > 0
+    cos = (o2[live] * r2[live]).sum(axis=1) / np.maximum(on[live] * rn[live], 1e-300)
+    big = np.abs(ref) >= 2e-3
+    stats = {
+        "max_abs": float(d.max()) if d.size else 0.0,
+        "max_rel": float((d[big] / np.abs(ref[big])).max()) if big.any() else 0.0,
+        "rel_l2": rel_l2,
+        "min_cos": float(cos.min()) if cos.size else 1.0,
+        "finite": bool(np.isfinite(out).all()),
+        "zero_rows_ok": bool(np.all(on[~live] == 0)),
+    }
+    if kind == "f32":
+        stats["ok"] = (stats["finite"] and stats["max_abs"] <= 2e-3 and stats["max_rel"] <= 2e-3
+                       and stats["rel_l2"] <= 1e-4 and stats["zero_rows_ok"])
+    elif kind == "lowp":
+        elem = bool(np.all(d <= 5e-3 + 5e-3 * np.abs(ref)))
+        stats["elementwise"] = elem
+        stats["ok"] = (stats["finite"] and elem and stats["rel_l2"] <= 1e-2
+                       and stats["min_cos"] >= 0.9999 and stats["zero_rows_ok"])
+    else:
+        raise ValueError(kind)
+    return stats
