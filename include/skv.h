@@ -1,0 +1,286 @@
+/*
+ * skv.h -- C ABI of the split-KV (flash-decoding) paged decode-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * A few query rows per request (one decode token, a speculative-verify block,
+ * or MTP rows) attend over a long KV cache that is contiguous or paged through
+ * a page table. The split-KV calls partition each request's visible key range
+ * into splits, run one workgroup per (split, KV head) that emits partial
+ * softmax statistics, and merge the splits in a second kernel.
+ *
+ * Sources, by page title and section:
+ *   [DR]  tiny-llm #11, "split-KV decode attention design record":
+ *         "Design" (partial kernel over (head, split) with chunk =
+ *         ceil(visible / splits) computed from a device visible length,
+ *         (m_i, l_i, acc_i) records, a combine kernel; host num_splits,
+ *         preallocated partial buffers, no allocation and no device-to-host
+ *         copy so calls stay graph-capturable; the single-pass entry points
+ *         keep num_splits = 1 semantics), "points for reviewer decision"
+ *         (Q1 separate combine kernel, Q2 host num_splits, Q3/Q4 the
+ *         single-split bitwise anchor exp(0) = 1 and 1/(l + 1e-9), Q5 the
+ *         caller may fall back to one split).
+ *   [VS]  hipfire #760, "split packed-Q8 verifier KV scans", Summary: the
+ *         causal prefix of a multi-row verifier split over 2/4/8 workgroups,
+ *         stable max-LSE merge; int8 ("Q8") KV; fail-closed admission.
+ *   [PA]  aiter #5628, "tune MTP work budgets and planned reduction":
+ *         intro and Changes (host work planner from host-known KV work,
+ *         per-request partition counts, capacity fixed for graph replay,
+ *         explicit budgets and caps take precedence, windowed work capped by
+ *         the causal-window union and tile alignment, reducer that iterates
+ *         only each request's actual partitions up to 256, sink
+ *         normalization, masked fallback, window checks); Performance (BF16
+ *         Q/O, FP8 KV with per-token FP32 scales, MTP4 causal rows, page
+ *         sizes 16 and 128, plain and transposed V).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  * All pointers in skv_args and skv_partials are DEVICE pointers; the
+ *    caller owns every buffer and the stream. No call allocates, frees,
+ *    synchronizes or copies device-to-host; every compute call only enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream), so all compute calls can be captured into a HIP graph.
+ *  * Every call validates its host arguments before enqueuing anything and
+ *    returns 0 on success or a negative SKV_ERR_* code; on error nothing was
+ *    enqueued (fail closed, [VS] Summary).
+ *  * Device values (context lengths, page-table entries) cannot be checked
+ *    without a device-to-host copy. Kernels clamp each context length to
+ *    [0, capacity] where capacity = max_pages * block_size (paged) or
+ *    kv_capacity (contiguous), and read only page-table entries
+ *    [0, ceil(ctx / block_size)) of a request. Entries there must be valid
+ *    page indices of the pool; an invalid index is undefined behaviour.
+ *
+ * Shapes and layouts (row-major, innermost last)
+ *   q, o          [B][R][Hq][D]   q_dtype (F32 or BF16); o has q's dtype,
+ *                                 bf16 results are rounded to nearest even.
+ *   paged k       [pages][Hkv][block_size][D]
+ *   paged v       PLAIN: as k;  TRANSPOSED: [pages][Hkv][D][block_size]
+ *   paged scales  [pages][Hkv][block_size] fp32 (INT8 / FP8 KV only; one
+ *                 scale per token per KV head for K and one for V)
+ *   contiguous k  [B][Hkv][kv_capacity][D]; v PLAIN as k, TRANSPOSED
+ *                 [B][Hkv][D][kv_capacity]; scales [B][Hkv][kv_capacity]
+ *   page_table    int32 [B][max_pages]: logical page i of request b is pool
+ *                 page page_table[b * max_pages + i]
+ *   ctx_lens      int32 [B] device visible lengths (the keys of a request,
+ *                 its R query tokens included)
+ *   sinks         fp32 [Hq] per-query-head sink logits (natural-log units)
+ *
+ * Semantics (readings of the pages, see the design notes of the repository)
+ *   Query head h uses KV head h / (Hq / Hkv). Causal row j of a request of
+ *   length ctx sits at position p_j = ctx - R + j (non-causal rows: ctx - 1)
+ *   and sees keys t in [0, ctx) with t <= p_j and, when window W > 0,
+ *   t > p_j - W. The logit of key t is x_t = scale * k_scale_t * <q, code_t>.
+ *   O = sum_t e^(x_t - M) v_t / (sum_t e^(x_t - M) [+ e^(sink_h - M)]).
+ *   A row that sees no key outputs 0 (with or without a sink).
+ *
+ * Split ranges ([DR] Design; [PA] Changes). For a request with S splits the
+ * split range is [u, ctx) where u = 0, or with a window the earliest row's
+ * window start aligned down to SKV_SPLIT_ALIGN; chunk = ceil((ctx - u) / S)
+ * rounded up to SKV_SPLIT_ALIGN; split s covers
+ * [u + s * chunk, min(u + (s + 1) * chunk, ctx)), possibly empty.
+ *
+ * Partial records (caller-owned scratch, [DR] Design / Q4). A record holds,
+ * for every one of the rho = R * Hq / Hkv query rows that share a KV head
+ * (row index r = j * (Hq / Hkv) + (h mod (Hq / Hkv))), three fp32 values of
+ * the split's visible keys T_s:
+ *   m   a reference maximum in log2 units, l = sum_{t in T_s} 2^(x_t log2(e) - m),
+ *   acc[D] = sum_{t in T_s} 2^(x_t log2(e) - m) v_t.
+ * (m is at least the largest x_t log2(e) - 8, so l and acc stay finite.)
+ * An empty T_s gives m = -inf, l = 0, acc = 0. Record slot numbers:
+ *   uniform splits:  slot = ((b * S) + s) * Hkv + g
+ *   planned splits:  slot = (req_slot0[b] + s) * Hkv + g
+ * and m[slot * rho + r], l[slot * rho + r], acc[(slot * rho + r) * D + d].
+ * The merge ([DR] Design, Q3; [PA] Changes): M = max over splits with l > 0
+ * (and the sink logit in log2 units); L = sum_s 2^(m_s - M) l_s
+ * (+ 2^(sink log2(e) - M)); O = (sum_s 2^(m_s - M) acc_s) * (1 / (L + 1e-9)),
+ * splits taken in increasing s. With one split this is bit-identical to the
+ * single-pass entry points.
+ */
+#ifndef SKV_H_
+#define SKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_ABI_VERSION 1
+#define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
+#define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
+
+/* Status codes. */
+#define SKV_OK 0
+#define SKV_ERR_NULL (-1)          /* a required pointer is NULL */
+#define SKV_ERR_SHAPE (-2)         /* B, R, Hq, Hkv, D, block size or strides out of range */
+#define SKV_ERR_DTYPE (-3)         /* unsupported dtype or dtype combination */
+#define SKV_ERR_SPLITS (-4)        /* num_splits < 1 or > SKV_MAX_SPLITS */
+#define SKV_ERR_CAPACITY (-5)      /* partial buffers hold too few records */
+#define SKV_ERR_UNSUPPORTED (-6)   /* valid request this build does not implement */
+#define SKV_ERR_LAUNCH (-7)        /* the HIP runtime rejected a kernel launch */
+#define SKV_ERR_PLAN (-8)          /* inconsistent plan hints or metadata sizes */
+
+typedef enum skv_dtype {
+  SKV_F32 = 0,
+  SKV_BF16 = 1,
+  SKV_INT8 = 2,       /* KV only: symmetric int8 codes times an fp32 scale */
+  SKV_FP8_E4M3 = 3    /* KV only: OCP e4m3fn codes times an fp32 scale */
+} skv_dtype;
+
+typedef enum skv_v_layout { SKV_V_PLAIN = 0, SKV_V_TRANSPOSED = 1 } skv_v_layout;
+
+/* Kernel family selection. AUTO picks the matrix-core kernel when q is BF16
+ * and KV is BF16, INT8 or FP8, else the vector kernel. */
+typedef enum skv_impl { SKV_IMPL_AUTO = 0, SKV_IMPL_VALU = 1, SKV_IMPL_MFMA = 2 } skv_impl;
+
+/* Host description of one call; fixed for the life of a captured graph. */
+typedef struct skv_desc {
+  int32_t batch;          /* B >= 1 */
+  int32_t q_rows;         /* R >= 1 query rows per request */
+  int32_t num_q_heads;    /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;       /* D in {64, 128, 256} */
+  int32_t causal;         /* 1: row j sits at ctx - R + j; 0: every row at ctx - 1 */
+  int32_t window;         /* sliding window W in keys, 0 = none */
+  float scale;            /* logit scale, usually 1/sqrt(D) */
+  int32_t q_dtype;        /* SKV_F32 or SKV_BF16 (o has the same dtype) */
+  int32_t kv_dtype;       /* skv_dtype */
+  int32_t block_size;     /* paged: tokens per page, power of two in [1, 1024] */
+  int32_t max_pages;      /* paged: page-table row stride (>= 1) */
+  int32_t kv_capacity;    /* contiguous: token stride per (request, KV head) */
+  int32_t v_layout;       /* skv_v_layout */
+  int32_t has_sink;       /* 1: args.sinks holds Hq fp32 logits */
+  int32_t impl;           /* skv_impl */
+} skv_desc;
+
+/* Device pointers of one call (k_scale / v_scale only for INT8 / FP8 KV,
+ * page_table only for paged calls, sinks only with has_sink). */
+typedef struct skv_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  const float* sinks;
+  void* o;
+} skv_args;
+
+/* Caller-owned partial-record buffers (device memory), sized by
+ * skv_workspace_size for `capacity_slots` records. */
+typedef struct skv_partials {
+  float* m;
+  float* l;
+  float* acc;
+  int64_t capacity_slots;
+} skv_partials;
+
+/* ---- version, status ---------------------------------------------------- */
+
+int skv_abi_version(void);
+/* Static string naming a status code; never NULL. */
+const char* skv_status_str(int status);
+
+/* ---- host-only checks and sizes (no HIP call; usable without a GPU) ------ */
+
+/* Validate a descriptor for a paged (paged = 1) or contiguous call with
+ * num_splits splits (0 = a single-pass call) and optional partial buffers.
+ * Returns SKV_OK or the error the corresponding compute call would return. */
+int skv_validate(const skv_desc* d, int32_t paged, int32_t num_splits, const skv_partials* p);
+
+/* Bytes of m, l and acc for `slots` partial records of descriptor d:
+ * slots * rho * 4, slots * rho * 4 and slots * rho * D * 4. Any output
+ * pointer may be NULL. */
+int skv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t* l_bytes,
+                       size_t* acc_bytes);
+
+/* Records needed by a uniform split call: B * num_splits * Hkv. */
+int64_t skv_uniform_slots(const skv_desc* d, int32_t num_splits);
+
+/* ---- single-pass entry points ([DR] Design: num_splits = 1 semantics) --- */
+
+/* Contiguous KV, one pass per (request, KV head); writes o. */
+int skv_attention_decode(const skv_desc* d, const skv_args* a, void* stream);
+/* Paged KV, one pass per (request, KV head); writes o. */
+int skv_attention_decode_paged(const skv_desc* d, const skv_args* a, void* stream);
+
+/* ---- split-KV entry points ([DR] Design) ---------------------------------
+ * num_splits is a host integer in [1, SKV_MAX_SPLITS], the same for every
+ * request; partials must hold skv_uniform_slots(d, num_splits) records.
+ * Enqueues the partial kernel and then the combine kernel. */
+int skv_attention_decode_splitkv(const skv_desc* d, const skv_args* a, int32_t num_splits,
+                                 const skv_partials* p, void* stream);
+int skv_attention_decode_paged_splitkv(const skv_desc* d, const skv_args* a, int32_t num_splits,
+                                       const skv_partials* p, void* stream);
+
+/* ---- host split planner ([PA] intro, Changes) -----------------------------
+ * The planner turns host-known context lengths into per-request partition
+ * counts P_b and a work list, written as an int32 metadata block that the
+ * caller copies to the device (e.g. hipMemcpyAsync from pinned memory on the
+ * compute stream) and passes to the planned call. Layout of the block:
+ *   [0] B   [1] capacity_items C   [2] num_items = sum_b P_b   [3] max_b P_b
+ *   [4, 4 + B)            P_b
+ *   [4 + B, 4 + 2B)       req_slot0[b] = sum_{b' < b} P_b'
+ *   [4 + 2B, 4 + 2B + C)  work item i: b * 256 + s, or -1 for an unused item
+ * Items are ordered longest first. A plan's capacity is fixed when it is
+ * made; refreshing it with new lengths keeps C (graph replay launches C
+ * items) and lowers partition counts if they would exceed it.
+ */
+typedef struct skv_plan_hints {
+  int32_t batch;                   /* B */
+  int32_t q_rows;                  /* R, the query length */
+  int32_t num_kv_heads;            /* Hkv */
+  int32_t causal;
+  int32_t window;                  /* 0 = none; work is capped by the causal-window union */
+  int32_t num_cus;                 /* 0 = 256 */
+  int32_t ctas_per_cu;             /* base occupancy budget per CU, 0 = 2 */
+  int32_t partitions_per_request;  /* > 0: explicit P_b for every request (precedence) */
+  int32_t max_partitions;          /* cap on P_b, 0 = SKV_MAX_SPLITS */
+  int32_t work_per_partition;      /* target key-rows (keys * R) per partition, 0 = 50000 */
+  int32_t min_tokens_per_partition;/* 0 = 256 */
+  int32_t reserved;
+  int64_t total_context_length;    /* optional work hint: sum of contexts to size capacity */
+} skv_plan_hints;
+
+typedef struct skv_plan_info {
+  int32_t num_items;       /* sum_b P_b */
+  int32_t capacity_items;  /* C */
+  int32_t max_partitions;  /* max_b P_b */
+  int32_t min_partitions;  /* min_b P_b */
+  int64_t slots;           /* C * Hkv partial records the planned call needs */
+} skv_plan_info;
+
+/* int32 entries of a metadata block for B requests and capacity C. */
+int64_t skv_plan_meta_len(int32_t batch, int32_t capacity_items);
+
+/* Capacity (items) a plan needs for these hints and host context lengths
+ * (host_ctx may be NULL when hints->total_context_length sizes it). */
+int skv_plan_capacity(const skv_plan_hints* h, const int32_t* host_ctx, int32_t* capacity_items);
+
+/* Make or refresh a plan: fill the host metadata block `meta` of `meta_len`
+ * int32 for capacity C from host context lengths. info may be NULL. */
+int skv_plan_fill(const skv_plan_hints* h, const int32_t* host_ctx, int32_t capacity_items,
+                  int32_t* meta, int64_t meta_len, skv_plan_info* info);
+
+/* Paged split-KV over a plan: plan_meta is the DEVICE copy of the block,
+ * capacity_items its C (the grid size), partials hold C * Hkv records. */
+int skv_attention_decode_paged_planned(const skv_desc* d, const skv_args* a,
+                                       const int32_t* plan_meta, int32_t capacity_items,
+                                       const skv_partials* p, void* stream);
+
+/* ---- the two stages on their own -----------------------------------------
+ * skv_splitkv_partial enqueues only the partial kernel, skv_splitkv_combine
+ * only the combine kernel; a split-KV call is exactly the two in order.
+ * plan_meta NULL selects uniform splits (num_splits); otherwise num_splits
+ * must be the plan's capacity C. */
+int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
+                        const int32_t* plan_meta, const skv_partials* p, void* stream);
+int skv_splitkv_combine(const skv_desc* d, const skv_args* a, int32_t num_splits,
+                        const int32_t* plan_meta, const skv_partials* p, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* SKV_H_ */

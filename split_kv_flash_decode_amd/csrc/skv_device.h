@@ -1,0 +1,159 @@
+// Device-side helpers shared by the HIP kernels: vector types, storage
+// conversions, address arithmetic of the KV layouts, wave reductions and the
+// split merge formula.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "skv_internal.h"
+
+namespace skv {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Storage tags.
+struct F32 {};
+struct BF16 {};
+struct I8 {};
+struct FP8 {};
+
+template <class T> struct Storage;
+template <> struct Storage<F32> { static constexpr int bytes = 4; static constexpr bool quant = false; };
+template <> struct Storage<BF16> { static constexpr int bytes = 2; static constexpr bool quant = false; };
+template <> struct Storage<I8> { static constexpr int bytes = 1; static constexpr bool quant = true; };
+template <> struct Storage<FP8> { static constexpr int bytes = 1; static constexpr bool quant = true; };
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t lo16) { return __uint_as_float(lo16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  floatx2 x = {a, b};
+  bf16x2 y = __builtin_convertvector(x, bf16x2);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+// Two e4m3fn codes (bytes 0-1 or, with HI, 2-3 of w) -> two fp32 values, exact.
+template <bool HI>
+__device__ __forceinline__ floatx2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Two e4m3fn codes -> packed bf16 pair, exact (every e4m3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  bf16x2 y = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+// Byte n of w as a signed int8 -> fp32 (exact).
+__device__ __forceinline__ float i8_to_f32(uint32_t w, int n) {
+  return (float)(int32_t)((int32_t)(w << (24 - 8 * n)) >> 24);
+}
+
+// ---- wave-wide reductions (butterflies: every lane ends with the same bits) --
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ---- KV addressing -----------------------------------------------------------
+// Element offset of K[token t][d] of KV head g of request b (row-major rows of D).
+__device__ __forceinline__ int64_t k_row(const Params& p, int page, int b, int g, int t) {
+  if (p.paged) {
+    int slot = t & ((1 << p.bs_shift) - 1);
+    return ((((int64_t)page * p.Hkv + g) << p.bs_shift) + slot) * p.D;
+  }
+  return (((int64_t)b * p.Hkv + g) * p.kv_cap + t) * p.D;
+}
+// Offset of scale of token t (paged [page][Hkv][bs], contiguous [B][Hkv][cap]).
+__device__ __forceinline__ int64_t scale_idx(const Params& p, int page, int b, int g, int t) {
+  if (p.paged) {
+    int slot = t & ((1 << p.bs_shift) - 1);
+    return (((int64_t)page * p.Hkv + g) << p.bs_shift) + slot;
+  }
+  return ((int64_t)b * p.Hkv + g) * p.kv_cap + t;
+}
+// Offset of V^T[d][t] in the transposed layouts ([page][Hkv][D][bs] or [B][Hkv][D][cap]).
+__device__ __forceinline__ int64_t vt_idx(const Params& p, int page, int b, int g, int d, int t) {
+  if (p.paged) {
+    int slot = t & ((1 << p.bs_shift) - 1);
+    return ((((int64_t)page * p.Hkv + g) * p.D + d) << p.bs_shift) + slot;
+  }
+  return (((int64_t)b * p.Hkv + g) * p.D + d) * p.kv_cap + t;
+}
+// Pool page holding token t of request b (paged), read only for t < ctx.
+__device__ __forceinline__ int page_of(const Params& p, int b, int t) {
+  return p.paged ? p.table[(int64_t)b * p.max_pages + (t >> p.bs_shift)] : 0;
+}
+
+__device__ __forceinline__ int clamp_ctx(const Params& p, int b) {
+  int c = p.ctx[b];
+  c = c < 0 ? 0 : c;
+  return c > p.cap ? p.cap : c;
+}
+
+// ---- the merge of split records ----------------------------------------------
+// One output element from one record (single pass). Written exactly like one
+// iteration of the combine kernel's loop so that a one-split combine gives the
+// same bits: M = max(m, sink); w = 2^(m - M); L = 0 + w l (+ 2^(sink - M));
+// O = (0 + w acc) * (1 / (L + 1e-9)); a record with l = 0 gives 0.
+__device__ __forceinline__ float finalize_one(float m, float l, float acc, int has_sink, float s2) {
+  if (!(l > 0.0f)) return 0.0f;
+  float M = fmaxf(-INFINITY, m);
+  if (has_sink) M = fmaxf(M, s2);
+  float L = 0.0f;
+  float a = 0.0f;
+  float w = fexp2(m - M);
+  L += w * l;
+  a += w * acc;
+  if (has_sink) L += fexp2(s2 - M);
+  float inv = 1.0f / (L + 1e-9f);
+  return a * inv;
+}
+
+// Output element store: fp32 or bf16 (RNE).
+__device__ __forceinline__ void store_o1(const Params& p, int64_t idx, float x) {
+  if (p.q_dtype == SKV_BF16) {
+    uint32_t w = pack_bf16x2(x, 0.0f);
+    reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)(w & 0xFFFF);
+  } else {
+    reinterpret_cast<float*>(p.o)[idx] = x;
+  }
+}
+
+__device__ __forceinline__ void store_o4(const Params& p, int64_t idx, floatx4 x) {
+  if (p.q_dtype == SKV_BF16) {
+    u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + idx) = w;
+  } else {
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(p.o) + idx) = x;
+  }
+}
+
+// Offset of q/o element [b][j][h][d].
+__device__ __forceinline__ int64_t qo_idx(const Params& p, int b, int j, int h, int d) {
+  return (((int64_t)b * p.R + j) * p.Hq + h) * p.D + d;
+}
+
+// Query row r (0 <= r < rho) of KV head g: query token j and head h.
+__device__ __forceinline__ void row_jh(const Params& p, int g, int r, int* j, int* h) {
+  *j = r / p.G;
+  *h = g * p.G + (r - (r / p.G) * p.G);
+}
+
+}  // namespace skv

@@ -1,0 +1,130 @@
+// Internal definitions shared by the host library and the HIP kernels.
+//
+// Nothing here is part of the C ABI; include/skv.h is.
+#pragma once
+
+#include <stdint.h>
+
+#include "skv.h"
+
+namespace skv {
+
+// Everything a kernel needs, passed by value as one kernel argument.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* ks;
+  const float* vs;
+  const int32_t* table;
+  const int32_t* ctx;
+  const float* sinks;
+  void* o;
+  float* pm;
+  float* pl;
+  float* pacc;
+  const int32_t* plan;   // device plan metadata, or nullptr for uniform splits
+  int32_t B, R, Hq, Hkv, D, G, rho;
+  int32_t causal, window;
+  float scale_log2;      // scale * log2(e)
+  int32_t bs_shift;      // log2(block_size) (paged)
+  int32_t max_pages;     // page-table row stride (paged)
+  int32_t cap;           // context clamp: max_pages * block_size or kv_capacity
+  int32_t kv_cap;        // contiguous token stride
+  int32_t num_splits;    // uniform S; with a plan, the plan capacity C
+  int32_t has_sink;
+  int32_t paged;
+  int32_t finalize;      // 1: single pass, write o instead of a partial record
+  int32_t n_items;       // work items in the grid
+  int32_t row_groups;    // row groups per (item, KV head)
+  int32_t q_dtype, kv_dtype, v_layout, block_size, impl;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSplitAlign = SKV_SPLIT_ALIGN;
+// Lazy rescaling: the running reference maximum is only raised when a new
+// logit exceeds it by more than this many powers of two.
+constexpr float kRescaleSlack = 8.0f;
+
+// Host + device helpers --------------------------------------------------------
+
+#if defined(__HIPCC__)
+#define SKV_HD __host__ __device__ __forceinline__
+#else
+#define SKV_HD inline
+#endif
+
+// Split s of S over the visible union of a request of length ctx:
+// [u, ctx) with u = 0 or the earliest row's window start aligned down;
+// chunk = ceil((ctx - u) / S) rounded up to kSplitAlign.
+SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, int* lo, int* hi) {
+  if (ctx <= 0) {
+    *lo = 0;
+    *hi = 0;
+    return;
+  }
+  int u = 0;
+  if (window > 0) {
+    int pmin = causal ? ctx - R : ctx - 1;
+    u = pmin - window + 1;
+    u = u < 0 ? 0 : u;
+    u = (u / kSplitAlign) * kSplitAlign;
+  }
+  int span = ctx - u;
+  int chunk = (span + S - 1) / S;
+  chunk = ((chunk + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
+  long long l0 = (long long)u + (long long)s * chunk;
+  if (l0 >= ctx) {
+    *lo = ctx;
+    *hi = ctx;
+    return;
+  }
+  long long h0 = l0 + chunk;
+  *lo = (int)l0;
+  *hi = (int)(h0 < ctx ? h0 : ctx);
+}
+
+// Visible key range [vlo, vhi) of query row j.
+SKV_HD void row_range(int ctx, int R, int causal, int window, int j, int* vlo, int* vhi) {
+  int p = causal ? ctx - R + j : ctx - 1;
+  int hi = p + 1;
+  if (hi > ctx) hi = ctx;
+  int lo = 0;
+  if (window > 0) lo = p - window + 1;
+  if (lo < 0) lo = 0;
+  if (hi < 0) hi = 0;
+  *vlo = lo;
+  *vhi = hi;
+}
+
+// Work item -> (request, split, splits of the request, record item index).
+struct Item {
+  int b, s, S, slot_item;
+};
+
+SKV_HD bool decode_item(const Params& p, int item, Item* it) {
+  if (p.plan) {
+    int w = p.plan[4 + 2 * p.B + item];
+    if (w < 0) return false;
+    it->b = w >> 8;
+    it->s = w & 255;
+    it->S = p.plan[4 + it->b];
+    it->slot_item = p.plan[4 + p.B + it->b] + it->s;
+  } else {
+    it->b = item / p.num_splits;
+    it->s = item - it->b * p.num_splits;
+    it->S = p.num_splits;
+    it->slot_item = item;
+  }
+  return true;
+}
+
+}  // namespace skv
+
+// Host-side launchers (defined in the .hip files) ---------------------------------
+namespace skv {
+int launch_partial_valu(Params p, void* stream);
+int launch_partial_mfma(Params p, void* stream);
+int launch_combine(Params p, void* stream);
+bool mfma_supported(const Params& p);
+}  // namespace skv
