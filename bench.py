@@ -1,0 +1,268 @@
+"""Split-KV paged decode-attention benchmark (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+                    [--block-size 16] [--v-layout plain] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: the host planner
+refreshes the plan from host-known context lengths and copies its metadata to
+the device, then the partial kernel and the combine kernel run (the timed
+step of aiter #5628 "tune MTP work budgets and planned reduction",
+Performance: plan refresh, attention and reduction on every call). Inputs are
+resident in HBM before timing starts. Prints one JSON line:
+
+  value       effective TB/s = logical bytes / time per step, where logical
+              bytes count Q and O, the valid K and V codes and their scales,
+              the referenced page-table entries and the context lengths once
+              (same page, Performance: the bandwidth note)
+  roofline    the partial kernel: algorithmic bytes per launch (264 B per
+              valid key per KV head for fp8 KV with two fp32 scales, i.e.
+              2 D + 8) over its mean launch time from HIP events around each
+              launch, against the 8 TB/s HBM peak; ``traffic`` is the HBM bytes
+              per launch measured with rocprofv3 counters (FETCH_SIZE +
+              WRITE_SIZE, scaled by a copy-kernel calibration) when a
+              committed measurement for the current kernel source exists
+  cpu_baseline  the fp64 oracle timed on host cores over a bounded sample of
+              the same workload (whole requests), as effective TB/s
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["skv_mfma.hip", "skv_device.h", "skv_internal.h", "skv_combine.hip"]
+
+
+def logical_bytes(ctx, *, R: int, Hq: int, Hkv: int, D: int, q_bytes: int, kv_bytes: int,
+                  quantized: bool, block_size: int, paged: bool = True) -> int:
+    """Effective bytes of one decode call: Q and O once, valid K and V codes,
+    their per-token per-KV-head fp32 scales, referenced page-table entries
+    (int32, ceil(ctx / bs) per request) and the int32 context lengths."""
+    B = len(ctx)
+    n = sum(int(c) for c in ctx)
+    qo = 2 * B * R * Hq * D * q_bytes
+    kv = 2 * n * Hkv * D * kv_bytes
+    sc = 2 * n * Hkv * 4 if quantized else 0
+    pt = 4 * sum(-(-int(c) // block_size) for c in ctx) if paged else 0
+    return qo + kv + sc + pt + 4 * B
+
+
+_DT = {"f32": 4, "bf16": 2, "int8": 1, "fp8": 1}
+
+
+def spec_bytes(spec) -> int:
+    return logical_bytes(spec.ctx, R=spec.R, Hq=spec.Hq, Hkv=spec.Hkv, D=spec.D,
+                         q_bytes=_DT[spec.q_dtype], kv_bytes=_DT[spec.kv_dtype],
+                         quantized=spec.kv_dtype in ("int8", "fp8"), block_size=spec.block_size)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "split_kv_flash_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per partial-kernel launch from a committed counter run, or None
+    when there is none for this workload or the kernel source changed since."""
+    path = os.path.join(PROFILES, "partial_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def workload_name(spec) -> str:
+    ctxs = sorted(set(spec.ctx))
+    ctx_s = f"ctx {spec.ctx[0]}" if len(ctxs) == 1 else f"ctx {spec.ctx[0]}+{len(spec.ctx) - 1}x{spec.ctx[-1]}"
+    return (f"B{spec.B} {ctx_s}, {'MTP' if spec.causal else 'R'}{spec.R} "
+            f"{'causal' if spec.causal else ''}, Hq{spec.Hq}/Hkv{spec.Hkv}/D{spec.D}, "
+            f"{spec.q_dtype} Q/O, {spec.kv_dtype} KV"
+            f"{' + per-token fp32 scales' if spec.kv_dtype in ('int8', 'fp8') else ''}, "
+            f"page {spec.block_size}, {spec.v_layout} V"
+            + (f", {spec.partitions_per_request} partitions/request" if spec.partitions_per_request else
+               ", planner partitions")
+            + (f", window {spec.window}" if spec.window else "") + (", sinks" if spec.sinks else ""))
+
+
+def cpu_baseline(problem, spec, budget_s: float = 12.0, max_requests: int = 200):
+    """Time the fp64 oracle on whole requests of the workload until ~budget_s."""
+    import threadpoolctl
+
+    import oracle
+    from skvgen import extract_request
+
+    done, t_oracle, nbytes = 0, 0.0, 0
+    for b in range(min(max_requests, spec.B)):
+        sub = extract_request(problem, b)
+        arrays = sub.host_arrays()
+        s = sub.spec
+        t = time.perf_counter()
+        oracle.decode_attention(arrays, R=s.R, Hq=s.Hq, Hkv=s.Hkv, D=s.D, causal=s.causal,
+                                window=s.window, scale=s.scale, q_dtype=s.q_dtype,
+                                kv_dtype=s.kv_dtype, paged=True, block_size=s.block_size,
+                                v_layout=s.v_layout, has_sink=s.sinks)
+        t_oracle += time.perf_counter() - t
+        nbytes += spec_bytes(sub.spec)
+        done += 1
+        if t_oracle >= budget_s:
+            break
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    return {
+        "value": round(nbytes / t_oracle / 1e12, 6),
+        "unit": "TB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {spec.B} requests (whole requests, {nbytes} logical bytes) in "
+                  f"{t_oracle:.2f} s; {t_oracle / done * spec.B * 1e6:.0f} us/step extrapolated",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--block-size", type=int, default=0)
+    ap.add_argument("--v-layout", default="")
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path needs no collectives; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import split_kv_flash_decode_amd as skv
+    from skvgen import config_spec, make_problem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    overrides = {}
+    if args.block_size:
+        overrides["block_size"] = args.block_size
+    if args.v_layout:
+        overrides["v_layout"] = args.v_layout
+    spec = config_spec(args.config, **overrides)
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {spec.name} on {dev} ...", file=sys.stderr, flush=True)
+    t = time.time()
+    p = make_problem(spec, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
+
+    o = torch.empty_like(p.q)
+    d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
+                      window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
+    a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
+                      page_table=p.page_table, sinks=p.sinks)
+    hints = skv.plan_hints(spec.B, spec.R, spec.Hkv, causal=spec.causal, window=spec.window,
+                           partitions_per_request=spec.partitions_per_request)
+    host_ctx = list(spec.ctx)
+    plan = skv.Plan(hints, host_ctx, dev)
+    ws = skv.Workspace(d, plan.info.slots, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        plan.refresh(host_ctx)
+        if ev is not None:
+            ev[0].record(stream)
+        skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
+        if ev is not None:
+            ev[1].record(stream)
+        skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = [e[0].elapsed_time(e[1]) for e in events]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes = spec_bytes(spec)
+    tbs = nbytes / (ms_per_step * 1e-3) / 1e12
+
+    unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
+    units = sum(int(c) for c in spec.ctx) * spec.Hkv
+    alg_bytes = unit_bytes * units
+    part_mean = sum(part_ms) / len(part_ms)
+    achieved = alg_bytes / (part_mean * 1e-3) / 1e9
+    key = f"cfg{args.config}_bs{spec.block_size}_{spec.v_layout}"
+    traffic = measured_traffic(key)
+
+    result = {
+        "metric": "decode-attention us/step + effective KV TB/s (fraction of HBM peak)",
+        "value": round(tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_fraction": round(tbs * 1e3 / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tbs / 4.607, 4) if (args.config == 4 and spec.block_size == 16
+                                                 and spec.v_layout == "plain") else None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload_name(spec),
+            "global_batch": spec.B,
+            "seq_len": max(spec.ctx),
+            "parallelism": "none (one GPU)",
+            "logical_bytes_per_step": nbytes,
+            "plan_items": plan.info.num_items,
+            "plan_capacity": plan.capacity,
+            "partial_us_mean": round(part_mean * 1e3, 2),
+            "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on host cores ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(p, spec, budget_s=args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/skv.h declares, arguments are validated before any
+launch, record sizes follow the documented layout, and the split planner
+reproduces the pages' example and its own invariants."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import split_kv_flash_decode_amd as skv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(skv.LIB_PATH):
+        from split_kv_flash_decode_amd import build
+        build.build()
+    return skv.lib()
+
+
+def test_library_exports_every_declared_function():
+    L = _lib()
+    with open(os.path.join(ROOT, "include", "skv.h")) as f:
+        text = f.read()
+    names = sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(skv_\w+)\(", text, re.M)))
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(L, n), f"{n} missing from libskv.so"
+    assert set(names) == set(skv.EXPORTS), "binding and header disagree"
+    assert skv.abi_version() == 1
+
+
+def _desc(**kw):
+    _lib()
+    q = torch.zeros(kw.pop("B", 2), kw.pop("R", 4), kw.pop("Hq", 16), kw.pop("D", 128),
+                    dtype=kw.pop("qdt", torch.bfloat16))
+    kdt = kw.pop("kdt", torch.uint8)
+    bs = kw.pop("bs", 16)
+    k = torch.zeros(8, kw.pop("Hkv", 1), bs, q.shape[-1], dtype=kdt)
+    d = skv.make_desc(q, k, k.clone(), paged=True, causal=True,
+                      page_table=torch.zeros(q.shape[0], 4, dtype=torch.int32), **kw)
+    return d
+
+
+def test_validation_codes():
+    d = _desc()
+    assert skv.validate(d, True, 0) == 0
+    assert skv.validate(d, True, 4) == -1                 # partials missing
+    bad = _desc()
+    bad.head_dim = 96
+    assert skv.validate(bad, True, 0) == -2
+    bad = _desc(Hkv=2)
+    bad.num_q_heads = 15
+    assert skv.validate(bad, True, 0) == -2
+    bad = _desc()
+    bad.block_size = 24
+    assert skv.validate(bad, True, 0) == -2
+    bad = _desc()
+    bad.kv_dtype = 7
+    assert skv.validate(bad, True, 0) == -3
+    bad = _desc()
+    bad.q_dtype = 2
+    assert skv.validate(bad, True, 0) == -3
+    assert skv.validate(_desc(), True, 257) == -4
+    assert skv.validate(_desc(), True, -1) == -4
+    f32 = _desc(qdt=torch.float32, kdt=torch.float32, impl="mfma")
+    assert skv.validate(f32, True, 0) == -6                # matrix-core path needs bf16 Q
+    small_page = _desc(bs=8, impl="mfma")
+    assert skv.validate(small_page, True, 0) == -6
+    assert skv.validate(_desc(bs=8), True, 0) == 0         # auto falls back to the vector kernel
+
+
+def test_partial_capacity_is_checked():
+    d = _desc()
+    need = skv.uniform_slots(d, 4)
+    assert need == 2 * 4 * 1
+    p = skv.Partials(1, 1, 1, need - 1)
+    assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == -5
+    p = skv.Partials(1, 1, 1, need)
+    assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == 0
+
+
+def test_compute_calls_fail_closed_without_launching():
+    d = _desc()
+    a = skv.Args()                                        # all NULL
+    L = skv.lib()
+    assert L.skv_attention_decode_paged(ctypes.byref(d), ctypes.byref(a), None) == -1
+    assert L.skv_attention_decode_paged_splitkv(ctypes.byref(d), ctypes.byref(a), 4, None, None) == -1
+    assert L.skv_attention_decode_paged(None, ctypes.byref(a), None) == -1
+    d.head_dim = 100
+    assert L.skv_attention_decode(ctypes.byref(d), ctypes.byref(a), None) == -2
+    for s in (0, -3, 1, -4, -8, 99):
+        assert isinstance(skv.status_str(s), str) and skv.status_str(s)
+
+
+def test_workspace_sizes():
+    d = _desc(B=3, R=4, Hq=16, Hkv=2, D=256)
+    m, l, acc = skv.workspace_size(d, 10)
+    rho = 4 * 8
+    assert m == l == 10 * rho * 4
+    assert acc == 10 * rho * 256 * 4
+
+
+# ---------------------------------------------------------------------------
+# planner
+
+def _plan(ctx, R=4, Hkv=1, capacity=None, **kw):
+    _lib()
+    h = skv.plan_hints(len(ctx), R, Hkv, **kw)
+    cap = capacity or skv.plan_capacity(h, ctx)
+    meta = torch.zeros(skv.plan_meta_len(len(ctx), cap), dtype=torch.int32)
+    info = skv.plan_fill(h, ctx, cap, meta)
+    return meta, info, cap
+
+
+def _decode(meta):
+    B, C, n, pmax = (int(x) for x in meta[:4])
+    P = meta[4:4 + B].tolist()
+    slot0 = meta[4 + B:4 + 2 * B].tolist()
+    work = meta[4 + 2 * B:4 + 2 * B + C].tolist()
+    return B, C, n, pmax, P, slot0, work
+
+
+def test_planner_reproduces_the_b200_example():
+    # aiter #5628, Changes: B200 / C200k / MTP4 selects 16 partitions per request, capacity 3200
+    meta, info, cap = _plan([200000] * 200)
+    B, C, n, pmax, P, slot0, work = _decode(meta)
+    assert cap == C == 3200 and n == 3200 and set(P) == {16}
+    assert info.slots == 3200 and info.max_partitions == 16 == info.min_partitions
+
+
+def test_planner_budget_floor_for_small_batches():
+    # intro of the same page: the base budget is two workgroups per CU (512 on 256 CUs)
+    meta, info, cap = _plan([200000] + [1024] * 15)
+    B, C, n, pmax, P, slot0, work = _decode(meta)
+    assert P[0] == 256                                    # the long request takes the budget, capped
+    assert all(2 <= p <= 4 for p in P[1:])
+    assert n == sum(P) <= C
+
+
+def test_planner_invariants_and_work_list():
+    import random
+    rng = random.Random(3)
+    for trial in range(30):
+        B = rng.randint(1, 40)
+        ctx = [rng.choice([0, 1, 63, 64, 65, 1000, 20676, 200000, rng.randint(0, 300000)]) for _ in range(B)]
+        R = rng.choice([1, 4, 16])
+        window = rng.choice([0, 0, 4096, 100])
+        meta, info, cap = _plan(ctx, R=R, Hkv=rng.choice([1, 2, 8]), window=window,
+                                partitions_per_request=rng.choice([0, 0, 3, 16]),
+                                max_partitions=rng.choice([0, 0, 7]))
+        B_, C, n, pmax, P, slot0, work = _decode(meta)
+        assert B_ == B and n == sum(P) and C == cap and pmax == max(P)
+        assert all(1 <= p <= 256 for p in P)
+        acc = 0
+        for b in range(B):
+            assert slot0[b] == acc
+            acc += P[b]
+            # never more partitions than 64-key tiles of the window-capped span
+            span = ctx[b] if window == 0 else min(ctx[b], window + R - 1 + 63)
+            assert P[b] <= max(1, -(-span // 64))
+        items = [w for w in work if w >= 0]
+        assert len(items) == n and all(w == -1 for w in work[n:])
+        assert sorted(items) == sorted(b * 256 + s for b in range(B) for s in range(P[b]))
+
+
+def test_explicit_partitions_and_caps_take_precedence():
+    meta, _, _ = _plan([200000] * 4, partitions_per_request=7)
+    assert _decode(meta)[4] == [7] * 4
+    meta, _, _ = _plan([200000] * 4, max_partitions=5)
+    assert _decode(meta)[4] == [5] * 4
+    meta, _, _ = _plan([100] * 4, partitions_per_request=7)
+    assert _decode(meta)[4] == [2] * 4                    # only two 64-key tiles
+
+
+def test_window_caps_planned_work():
+    meta, _, _ = _plan([200000], window=4096, min_tokens_per_partition=256)
+    P = _decode(meta)[4]
+    assert P[0] <= -(-(4096 + 3 + 63) // 256)
+
+
+def test_refresh_keeps_capacity():
+    _lib()
+    h = skv.plan_hints(8, 4, 1)
+    cap = skv.plan_capacity(h, [1000] * 8)
+    meta = torch.zeros(skv.plan_meta_len(8, cap), dtype=torch.int32)
+    info = skv.plan_fill(h, [200000] * 8, cap, meta)          # much longer contexts, same capacity
+    B, C, n, pmax, P, slot0, work = _decode(meta)
+    assert C == cap and n <= cap and info.num_items == n
+    with pytest.raises(skv.SkvError):
+        skv.plan_fill(h, [1000] * 8, 7, torch.zeros(skv.plan_meta_len(8, 7), dtype=torch.int32))
