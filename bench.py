@@ -146,6 +146,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 1 GiB device-to-device copies (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -160,6 +162,17 @@ def main(argv=None) -> int:
     from skvgen import config_spec, make_problem
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        # A plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of these
+        # dispatches give the counter-to-bytes factor used for ``traffic``.
+        n = 1 << 28                                     # 2^28 fp32 = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 4 * n, "copies": 3}), flush=True)
+        return 0
     overrides = {}
     if args.block_size:
         overrides["block_size"] = args.block_size

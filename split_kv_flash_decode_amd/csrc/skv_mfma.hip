@@ -34,6 +34,8 @@
 //    multiply-by-zero, so NaN-poisoned cache slots past a request's context
 //    never reach an accumulator) and zero V bytes of keys past the split.
 
+#include <type_traits>
+
 #include "skv_device.h"
 
 namespace skv {
@@ -92,44 +94,84 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int first, int nv, in
 
 }  // namespace
 
+// Wait until at most n vector-memory operations of this wave are outstanding.
+// Direct-to-LDS loads count in vmcnt; the compiler does not order later LDS
+// reads after them, so every stage is consumed after an explicit wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// One direct-to-LDS load per lane (16 or 4 bytes): lane l's bytes land at
+// lds + l * size. Issued as inline assembly so that the compiler neither
+// reorders LDS reads around it nor adds its own (draining) waits; every
+// consumer waits with wait_vm.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Page-table entry read through the constant address space: the table is
+// read-only for the whole call, so uniform reads become scalar loads.
+__device__ __forceinline__ int cload(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 template <class KT, int D, int NRB, bool VT>
 __global__ __launch_bounds__(256) void partial_mfma(Params p) {
   constexpr int EB = Storage<KT>::bytes;
   constexpr bool QUANT = Storage<KT>::quant;
-  constexpr int TB = (D * EB <= 128 && NRB == 1) ? 2 : 1;   // 32-key blocks per tile
-  constexpr int T = 32 * TB;                     // keys per tile
   constexpr int KS = D / 16;                     // Q.K^T k-steps of 16 d
   constexpr int DB = D / 32;                     // P.V d-blocks of 32
-  constexpr int KW = D * EB / 8;                 // dwords of a lane's half K row
   constexpr int ROWS = 32 * NRB;
-  constexpr int PD = D + 1;                      // LDS row stride (floats)
-  constexpr int VTW = 4 * EB;                    // dwords of 16 transposed keys
-  constexpr int VB = (D / 32) * EB;              // bytes of a plain V chunk per key
-  constexpr int VPW = VB >= 4 ? VB / 4 : 1;      // dwords of that chunk
-  constexpr int VW = VT ? DB * VTW : 16 * VPW;   // V dwords per key block per lane
-  constexpr bool PF = TB * (KW + VW) <= 64;      // double-buffer raw tiles in registers
+  constexpr int RB = D * EB;                     // bytes of one key row
+  constexpr int NCH = RB / 32;                   // 1 KiB load chunks of K (and of V) per 32-key block
+  constexpr int NI = 2 * NCH + (QUANT ? 1 : 0);  // direct-to-LDS loads per block
+  // Stage: K rows (32 RB bytes), V (plain: two 16-key groups of rows, the
+  // second shifted by 128 bytes so the two lane halves read different LDS
+  // banks; transposed: 16-byte key runs of V^T rows), then 32 K and 32 V
+  // scales.
+  constexpr int KSZ = 32 * RB;
+  constexpr int VGS = 16 * RB + 128;             // plain V: group stride
+  constexpr int VSZ = VT ? 32 * RB : 2 * VGS;
+  constexpr int STAGE = KSZ + VSZ + (QUANT ? 256 : 0);
+  constexpr int KIG = RB / 64;                   // 1 KiB loads per 16-key group, K (and plain V)
+  constexpr int U = DB * EB;                     // transposed V: 512-byte units per group
+  static_assert(RB >= 64 && RB % 64 == 0, "key rows of 64, 128 or 256 bytes");
+  constexpr int QS = D + 8;                      // LDS row stride of Q (bf16), padded
+  constexpr int QBYTES = ROWS * QS * 2;
+  constexpr int BUDGET = 156 * 1024;
+  constexpr int NS0 = (BUDGET - QBYTES) / (4 * STAGE);
+  constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per wave
+  constexpr int RING = 4 * NS * STAGE;
+  constexpr int PD = D + 1;                      // merge buffer row stride (floats)
+  constexpr int MERGE = ROWS * PD * 4;
+  constexpr int SMEM0 = RING > MERGE ? RING : MERGE;
+  constexpr int VB = (D / 32) * EB;              // plain V: bytes of a lane's d chunk per key
 
-  struct Raw {
-    uint32_t k[TB][KW];
-    uint32_t v[TB][VW];
-    float sk, sv;
-  };
-  struct Ids {       // pool pages of the tile's keys (page size >= 16, tile <= 64 keys)
-    int p0, p1, p2, p3;
-  };
-
-  __shared__ float acc_s[ROWS * PD];
+  __shared__ __attribute__((aligned(16))) char smem[SMEM0 + QBYTES];
   __shared__ float ml_s[4][ROWS][2];
   __shared__ float fin_s[ROWS][2];
-  __shared__ float sc_s[4][2][T];
-  constexpr int QS = D + 8;                      // LDS row stride of Q (bf16), padded
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[ROWS * QS];
+  uint16_t* q_s = reinterpret_cast<uint16_t*>(smem + SMEM0);
+  float* acc_s = reinterpret_cast<float*>(smem);   // reused after the key loop
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int i32 = lane & 31;
   const int hh = lane >> 5;
+  char* ring = smem + w * NS * STAGE;
 
   int blk = blockIdx.x;
   const int rg = blk % p.row_groups;
@@ -167,16 +209,16 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
     vhi[rb] = 0;
     if (r < p.rho) row_range(ctx, p.R, p.causal, p.window, r / p.G, &vlo[rb], &vhi[rb]);
   }
-  __syncthreads();
   // Keys every row of the group sees: [ilo, ihi).
   int ilo, ihi;
   {
     int a0, a1, c0, c1;
     row_range(ctx, p.R, p.causal, p.window, rbase / p.G, &a0, &a1);
     row_range(ctx, p.R, p.causal, p.window, (rbase + nrow - 1) / p.G, &c0, &c1);
-    ilo = a0 > c0 ? a0 : c0;
-    ihi = a1 < c1 ? a1 : c1;
+    ilo = __builtin_amdgcn_readfirstlane(a0 > c0 ? a0 : c0);
+    ihi = __builtin_amdgcn_readfirstlane(a1 < c1 ? a1 : c1);
   }
+  __syncthreads();
 
   floatx16 acc[NRB][DB];
   float mrun[NRB], lrun[NRB];
@@ -193,121 +235,225 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
   const int* trow = p.paged ? p.table + (int64_t)b * p.max_pages : nullptr;
-  const int bs_mask = (1 << p.bs_shift) - 1;
 
-  // Page ids of the tile at t0 (scalar loads; entries past the split are not read).
+  struct Ids {       // pool pages of a 32-key block's two halves (page size >= 16)
+    int p0, p1;
+  };
   auto load_ids = [&](int t0) __attribute__((always_inline)) {
-    Ids id{0, 0, 0, 0};
+    Ids id{0, 0};
     if (p.paged) {
-      const int base = t0 >> p.bs_shift;
-      const int bs = 1 << p.bs_shift;
-      id.p0 = trow[base];
-      id.p1 = (bs < T && t0 + bs < hi) ? trow[base + 1] : id.p0;
-      id.p2 = (2 * bs < T && t0 + 2 * bs < hi) ? trow[base + 2] : id.p0;
-      id.p3 = (3 * bs < T && t0 + 3 * bs < hi) ? trow[base + 3] : id.p0;
+      id.p0 = cload(trow + (t0 >> p.bs_shift));
+      id.p1 = (p.bs_shift == 4 && t0 + 16 < hi) ? cload(trow + (t0 >> 4) + 1) : id.p0;
     }
     return id;
   };
-  auto pick = [&](const Ids& id, int kk) __attribute__((always_inline)) {
-    const int x = kk >> p.bs_shift;
-    const int a = (x & 1) ? id.p1 : id.p0;
-    const int c = (x & 1) ? id.p3 : id.p2;
-    return (x & 2) ? c : a;
+  // Row index of the first key of 16-key group gp of the block at t0 (keys of
+  // a group are consecutive rows of one page): K and plain V rows are at
+  // base + R * RB, scales at scale + R. A group that starts at or past hi
+  // reuses group 0 (inside the split), so no page past the request's context
+  // is addressed; keys past hi inside a live group stay inside their page.
+  auto grp_row = [&](const Ids& id, int t0, int gp) __attribute__((always_inline)) {
+    const int tg = (t0 + 16 * gp < hi) ? t0 + 16 * gp : t0;
+    if (p.paged) {
+      const int pg = (gp && p.bs_shift == 4 && t0 + 16 < hi) ? id.p1 : id.p0;
+      return (((int64_t)pg * p.Hkv + g) << p.bs_shift) + (tg & ((1 << p.bs_shift) - 1));
+    }
+    return ((int64_t)b * p.Hkv + g) * p.kv_cap + tg;
   };
-  // Raw K, V codes and scales of the tile at t0. Keys at or past hi are
-  // redirected to key t0 (inside the split) so that no page past the
-  // request's context is ever addressed.
-  auto load_raw = [&](int t0, const Ids& id) __attribute__((always_inline)) {
-    Raw r;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      int kk = tb * 32 + tau(i32);
-      if (t0 + kk >= hi) kk = 0;
-      const char* src = kbase + (k_row(p, pick(id, kk), b, g, t0 + kk) + hh * (D / 2)) * EB;
-#pragma unroll
-      for (int c = 0; c < KW / 4; ++c) {
-        const u32x4 x = ld16(src + 16 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r.k[tb][4 * c + e] = x[e];
-      }
-      if constexpr (VT) {
-        int gk = tb * 32 + 16 * hh;
-        if (t0 + gk >= hi) gk = 0;
-        const int pg = pick(id, gk);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* vs = vbase + vt_idx(p, pg, b, g, 32 * db + i32, t0 + gk) * EB;
-#pragma unroll
-          for (int c = 0; c < VTW / 4; ++c) {
-            const u32x4 x = ld16(vs + 16 * c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) r.v[tb][db * VTW + 4 * c + e] = x[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int kv = tb * 32 + 16 * hh + e;
-          if (t0 + kv >= hi) kv = 0;
-          const char* vs = vbase + (k_row(p, pick(id, kv), b, g, t0 + kv) + (D / 32) * i32) * EB;
-          if constexpr (VB == 2) {
-            r.v[tb][e] = *reinterpret_cast<const uint16_t*>(vs);
-          } else if constexpr (VB == 4) {
-            r.v[tb][e] = *reinterpret_cast<const uint32_t*>(vs);
-          } else if constexpr (VB == 8) {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(vs);
-            r.v[tb][2 * e] = x[0];
-            r.v[tb][2 * e + 1] = x[1];
-          } else {
-            const u32x4 x = ld16(vs);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) r.v[tb][4 * e + q] = x[q];
-          }
-        }
-      }
+  // Transposed V: element index of V^T row 0 at the group's first key.
+  auto grp_vt = [&](const Ids& id, int t0, int gp) __attribute__((always_inline)) {
+    const int tg = (t0 + 16 * gp < hi) ? t0 + 16 * gp : t0;
+    if (p.paged) {
+      const int pg = (gp && p.bs_shift == 4 && t0 + 16 < hi) ? id.p1 : id.p0;
+      return ((((int64_t)pg * p.Hkv + g) * D) << p.bs_shift) + (tg & ((1 << p.bs_shift) - 1));
     }
-    if constexpr (QUANT) {
-      int kk = lane & (T - 1);
-      if (t0 + kk >= hi) kk = 0;
-      const int64_t si = scale_idx(p, pick(id, kk), b, g, t0 + kk);
-      r.sk = p.ks[si];
-      r.sv = p.vs[si];
-    } else {
-      r.sk = 1.0f;
-      r.sv = 1.0f;
-    }
-    return r;
+    return (((int64_t)b * p.Hkv + g) * D) * p.kv_cap + tg;
   };
 
-  auto compute = [&](const Raw& r, int t0) __attribute__((always_inline)) {
-    const bool interior = (t0 + T <= hi) && (t0 >= ilo) && (t0 + T <= ihi);
-    if constexpr (QUANT) {
-      if (lane < T) {
-        sc_s[w][0][lane] = r.sk * p.scale_log2;
-        sc_s[w][1][lane] = r.sv;
+  // Per-lane byte offsets of the direct-to-LDS loads (fixed for the kernel).
+  //  K, group gp, load n: lane l fetches 16 bytes of key (l % 16) ^ (8 gp) of
+  //    the group at row byte (4 n + l / 16) * 16; the XOR spreads the
+  //    consumer's 16-byte LDS reads over all banks.
+  //  plain V, load n: row n * (1024 / RB) + l / (RB / 16), 16-byte column
+  //    l % (RB / 16) (the group's rows, in key order).
+  //  transposed V, load n: unit u = 2 n + l / 32 (d-block u / EB, 16-byte key
+  //    run u % EB) of V^T row d = 32 (u / EB) + l % 32.
+  uint32_t koffs[2][KIG];
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int n = 0; n < KIG; ++n)
+      koffs[gp][n] = (uint32_t)(((lane & 15) ^ (8 * gp)) * RB + (4 * n + (lane >> 4)) * 16);
+  constexpr int NVL = VT ? U / 2 : KIG;          // V loads per group
+  uint32_t voffs[NVL];
+  {
+    const int dstride = (p.paged ? (1 << p.bs_shift) : p.kv_cap) * EB;
+#pragma unroll
+    for (int n = 0; n < NVL; ++n) {
+      if constexpr (VT) {
+        const int u = 2 * n + (lane >> 5);
+        voffs[n] = (uint32_t)((32 * (u / EB) + i32) * dstride + (u % EB) * 16);
+      } else {
+        constexpr int LPR = RB / 16;
+        voffs[n] = (uint32_t)((n * (1024 / RB) + lane / LPR) * RB + (lane % LPR) * 16);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+
+  // Issue the direct-to-LDS loads of the 32-key block at t0 into stage st.
+  auto issue = [&](int t0, const Ids& id, int st) __attribute__((always_inline)) {
+    const uint32_t S = lds_addr(ring + st * STAGE);
+    const int64_t R0 = grp_row(id, t0, 0), R1 = grp_row(id, t0, 1);
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const char* kb = kbase + (gp ? R1 : R0) * RB;
+#pragma unroll
+      for (int n = 0; n < KIG; ++n) dma16s(kb, koffs[gp][n], S + (gp * KIG + n) * 1024);
+    }
+    if constexpr (VT) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const char* vb = vbase + grp_vt(id, t0, gp) * EB;
+#pragma unroll
+        for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + (gp * NVL + n) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const char* vb = vbase + (gp ? R1 : R0) * RB;
+#pragma unroll
+        for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + gp * VGS + n * 1024);
+      }
+    }
+    if constexpr (QUANT) {
+      // lane l < 32: K scale of key l; l >= 32: V scale of key l - 32
+      const int k = i32;
+      const int64_t r = ((k >= 16) ? R1 : R0) + (k & 15);
+      dma4((hh ? p.vs : p.ks) + r, S + KSZ + VSZ);
+    }
+  };
+
+  // Consumer side of the K layout: key tau(i32) sits in group tau / 16 at
+  // position (tau % 16) ^ (8 group); its 16-byte chunk j of the row is at
+  // + j * 256.
+  const int kread = ((tau(i32) >> 4) * KIG) * 1024 + ((tau(i32) & 15) ^ (8 * (tau(i32) >> 4))) * 16;
+
+  // Logits of one 32-key block: t = s * c - mu, with c = scale * log2(e) *
+  // k_scale and mu the running reference maximum, so that the probability is
+  // exp2(t). MASK selects the boundary version (causal / window / split end by
+  // select, never by multiplying with zero). Returns whether a row's reference
+  // must rise (a logit more than 2^8 above it).
+  auto logits = [&](auto mask_tag, floatx16 (&s)[NRB], const float (&c)[16], int t0, int kb,
+                    float (&mloc)[NRB]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bool need = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mu = (mrun[rb] == -INFINITY) ? 0.0f : mrun[rb];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float t = __builtin_fmaf(s[rb][v], c[v], -mu);
+        if constexpr (MASK) {
+          const int k = t0 + kb + v;
+          const bool vis = (k < hi) & (k >= vlo[rb]) & (k < vhi[rb]);
+          t = vis ? t : -INFINITY;
+        }
+        s[rb][v] = t;
+        mx = fmaxf(mx, t);
+      }
+      mloc[rb] = mx;
+      need |= (mrun[rb] == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+    }
+    return need;
+  };
+  // Probabilities times the V scale as the bf16 P^T operand; l accumulates.
+  auto probs = [&](auto mask_tag, const floatx16 (&s)[NRB], const float (&sv)[16],
+                   bf16x8 (&pf)[NRB][2]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float lsum = 0.0f;
+      float pv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pe = fexp2(s[rb][v]);
+        lsum += pe;
+        if constexpr (QUANT) {
+          if constexpr (MASK) {
+            pv[v] = pe > 0.0f ? pe * sv[v] : 0.0f;    // NaN scales of masked keys stay out
+          } else {
+            pv[v] = pe * sv[v];
+          }
+        } else {
+          pv[v] = pe;
+        }
+      }
+      lrun[rb] += lsum;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const u32x4 pk = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
+                          pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]), pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
+        pf[rb][kh] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+  };
+  // Raise the references of rows whose logits exceeded them (rare: the wave
+  // votes first); alpha = 1 and shift = 0 leave the other rows unchanged.
+  auto rescale = [&](floatx16 (&s)[NRB], const float (&mloc)[NRB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float mu = (mrun[rb] == -INFINITY) ? 0.0f : mrun[rb];
+      const float mt = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 32, 64));   // row max - mu
+      const float mnew = fmaxf(mrun[rb], mt + mu);
+      const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun[rb] - mnew);   // 0 when mrun = -inf
+      const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
+      lrun[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rb][db][v] *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[rb][v] -= shift;
+      mrun[rb] = mnew;
     }
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int kb = tb * 32 + 16 * hh;        // first key (in the tile) of this lane's 16
-      // ---- S^T = K Q^T for this 32-key block
-      floatx16 s[NRB];
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
+  };
+
+  auto compute = [&](int t0, int st) __attribute__((always_inline)) {
+    const char* S = ring + st * STAGE;
+    const bool interior =
+        __builtin_amdgcn_readfirstlane((int)((t0 + 32 <= hi) && (t0 >= ilo) && (t0 + 32 <= ihi))) != 0;
+    const int kb = 16 * hh;                       // first key of this lane's 16
+    // ---- S^T = K Q^T for this 32-key block
+    floatx16 s[NRB];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[rb][v] = 0.0f;
-      int qoff = i32 * QS + hh * (D / 2);
-      asm volatile("" : "+v"(qoff));          // re-read Q from LDS every block
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+      for (int v = 0; v < 16; ++v) s[rb][v] = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(s[rb]));
+    int qoff = i32 * QS + hh * (D / 2);
+    asm volatile("" : "+v"(qoff));                // re-read Q from LDS every block
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4 kc = *reinterpret_cast<const u32x4*>(S + kread + (hh * NCH + c) * 256);
+      constexpr int KPC = 16 / (8 * EB);          // k-steps per 16-byte chunk
+#pragma unroll
+      for (int h2 = 0; h2 < KPC; ++h2) {
+        const int kk = c * KPC + h2;
         bf16x8 kf;
         if constexpr (EB == 1) {
-          kf = cvt8<KT>(r.k[tb][2 * kk], r.k[tb][2 * kk + 1], 0u, 0u);
+          kf = cvt8<KT>(kc[2 * h2], kc[2 * h2 + 1], 0u, 0u);
         } else {
-          kf = cvt8<KT>(r.k[tb][4 * kk], r.k[tb][4 * kk + 1], r.k[tb][4 * kk + 2], r.k[tb][4 * kk + 3]);
+          kf = cvt8<KT>(kc[0], kc[1], kc[2], kc[3]);
         }
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -315,147 +461,144 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
           s[rb] = mfma(kf, qf, s[rb]);
         }
       }
-      // ---- logits and masks
-      float c[16], sv[16];
-      if constexpr (QUANT) {
+    }
+    // S feeds VALU code: keep it in VGPRs (the MFMA writes them directly).
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const floatx4 a = *reinterpret_cast<const floatx4*>(&sc_s[w][0][kb + 4 * q]);
-          const floatx4 z = *reinterpret_cast<const floatx4*>(&sc_s[w][1][kb + 4 * q]);
+    for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(s[rb]));
+    // ---- per-key scales (K scale folded into c, V scale into the probabilities)
+    float c[16], sv[16];
+    if constexpr (QUANT) {
+      const float* sc = reinterpret_cast<const float*>(S + KSZ + VSZ);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            c[4 * q + e] = a[e];
-            sv[4 * q + e] = z[e];
-          }
-        }
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(sc + kb + 4 * q);
+        const floatx4 z = *reinterpret_cast<const floatx4*>(sc + 32 + kb + 4 * q);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          c[v] = p.scale_log2;
-          sv[v] = 1.0f;
+        for (int e = 0; e < 4; ++e) {
+          c[4 * q + e] = a[e] * p.scale_log2;
+          sv[4 * q + e] = z[e];
         }
       }
-      float mloc[NRB];
-      bool need = false;
+    } else {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[rb][v] * c[v];
-          if (!interior) {
-            const int t = t0 + kb + v;
-            const bool vis = t < hi && t >= vlo[rb] && t < vhi[rb];
-            x = vis ? x : -INFINITY;
-          }
-          s[rb][v] = x;
-          mx = fmaxf(mx, x);
-        }
-        mloc[rb] = mx;
-        need |= mx > mrun[rb] + kRescaleSlack;
+      for (int v = 0; v < 16; ++v) {
+        c[v] = p.scale_log2;
+        sv[v] = 1.0f;
       }
-      // ---- lazy rescale: raise the reference max only when it is exceeded by > 2^8
-      if (__any(need)) {
+    }
+    float mloc[NRB];
+    const bool need = interior ? logits(std::false_type{}, s, c, t0, kb, mloc)
+                               : logits(std::true_type{}, s, c, t0, kb, mloc);
+    if (__any(need)) rescale(s, mloc);
+    bf16x8 pf[NRB][2];
+    if (interior)
+      probs(std::false_type{}, s, sv, pf);
+    else
+      probs(std::true_type{}, s, sv, pf);
+    // ---- O^T += V^T P^T
+    const int nv = hi - (t0 + kb);                // keys of this lane's 16 inside the split
+    if constexpr (VT) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const float mt = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 32, 64));
-          const float mnew = fmaxf(mrun[rb], mt);
-          const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
-          const float alpha = fexp2(mrun[rb] - mu);
-          lrun[rb] *= alpha;
+      for (int db = 0; db < DB; ++db) {
+        uint32_t x[4 * EB];
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+        for (int e = 0; e < EB; ++e) {
+          const u32x4 vc = *reinterpret_cast<const u32x4*>(S + KSZ + hh * U * 512 + (db * EB + e) * 512 + i32 * 16);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[rb][db][v] *= alpha;
-          mrun[rb] = mnew;
+          for (int q = 0; q < 4; ++q) x[4 * e + q] = vc[q];
         }
-      }
-      // ---- probabilities (times the V scale) as the bf16 P^T operand
-      bf16x8 pf[NRB][2];
+        if (!interior) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float mu = (mrun[rb] == -INFINITY) ? 0.0f : mrun[rb];
-        float lsum = 0.0f;
-        float pv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float pe = fexp2(s[rb][v] - mu);
-          lsum += pe;
-          if constexpr (QUANT) {
-            pv[v] = interior ? pe * sv[v] : (pe > 0.0f ? pe * sv[v] : 0.0f);
-          } else {
-            pv[v] = pe;
-          }
+          for (int q = 0; q < 4 * EB; ++q) x[q] = keep_bytes(x[q], q * (4 / EB), nv, 4 / EB);
         }
-        lrun[rb] += lsum;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const u32x4 pk = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
-                            pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]), pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
-          pf[rb][kh] = __builtin_bit_cast(bf16x8, pk);
-        }
-      }
-      // ---- O^T += V^T P^T
-      const int nv = hi - (t0 + kb);          // keys of this lane's 16 inside the split
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
           bf16x8 vf;
-          if constexpr (VT) {
-            uint32_t x[4];
-            if constexpr (EB == 1) {
-#pragma unroll
-              for (int c2 = 0; c2 < 2; ++c2) {
-                const int wi = 2 * kh + c2;
-                x[c2] = interior ? r.v[tb][db * VTW + wi] : keep_bytes(r.v[tb][db * VTW + wi], 4 * wi, nv, 4);
-              }
-              vf = cvt8<KT>(x[0], x[1], 0u, 0u);
-            } else {
-#pragma unroll
-              for (int c2 = 0; c2 < 4; ++c2) {
-                const int wi = 4 * kh + c2;
-                x[c2] = interior ? r.v[tb][db * VTW + wi] : keep_bytes(r.v[tb][db * VTW + wi], 2 * wi, nv, 2);
-              }
-              vf = cvt8<KT>(x[0], x[1], x[2], x[3]);
-            }
+          if constexpr (EB == 1) {
+            vf = cvt8<KT>(x[2 * kh], x[2 * kh + 1], 0u, 0u);
           } else {
-            const int wi = (EB == 1) ? (db >> 2) : (db >> 1);
-            u32x4 rr;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              rr[u] = vpair<KT>(r.v[tb][(8 * kh + 2 * u) * VPW + wi], r.v[tb][(8 * kh + 2 * u + 1) * VPW + wi], db);
-            vf = __builtin_bit_cast(bf16x8, rr);
+            vf = cvt8<KT>(x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]);
           }
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) acc[rb][db] = mfma(vf, pf[rb][kh], acc[rb][db]);
         }
       }
+    } else {
+      constexpr int VPW = VB >= 4 ? VB / 4 : 1;
+      uint32_t vr[16][VPW];
+      const char* vrow = S + KSZ + hh * VGS + VB * i32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const char* src = vrow + e * RB;
+        if constexpr (VB == 2) {
+          vr[e][0] = *reinterpret_cast<const uint16_t*>(src);
+        } else if constexpr (VB == 4) {
+          vr[e][0] = *reinterpret_cast<const uint32_t*>(src);
+        } else if constexpr (VB == 8) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+          vr[e][0] = x[0];
+          vr[e][1] = x[1];
+        } else {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) vr[e][q] = x[q];
+        }
+      }
+      if (!interior) {                            // keys past the split may be NaN-poisoned
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+#pragma unroll
+          for (int q = 0; q < VPW; ++q) vr[e][q] = (e < nv) ? vr[e][q] : 0u;
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int wi = (EB == 1) ? (db >> 2) : (db >> 1);
+          u32x4 rr;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rr[u] = vpair<KT>(vr[8 * kh + 2 * u][wi], vr[8 * kh + 2 * u + 1][wi], db);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, rr);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) acc[rb][db] = mfma(vf, pf[rb][kh], acc[rb][db]);
+        }
+      }
     }
+    // The accumulators only meet VALU code in the rare rescale and at the
+    // end: keep them in AGPRs across blocks.
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
   };
 
-  const int ntiles = hi > lo ? (hi - lo + T - 1) / T : 0;
-  if constexpr (PF) {
-    int ti = w;
-    Raw cur, nxt;
-    Ids ids2;
-    if (ti < ntiles) cur = load_raw(lo + ti * T, load_ids(lo + ti * T));
-    if (ti + 4 < ntiles) ids2 = load_ids(lo + (ti + 4) * T);
-    for (; ti < ntiles; ti += 4) {
-      const int t0 = lo + ti * T;
-      const bool has1 = ti + 4 < ntiles;
-      const bool has2 = ti + 8 < ntiles;
-      if (has1) nxt = load_raw(t0 + 4 * T, ids2);
-      if (has2) ids2 = load_ids(t0 + 8 * T);
-      compute(cur, t0);
-      if (has1) cur = nxt;
-    }
-  } else {
-    for (int ti = w; ti < ntiles; ti += 4) {
-      const int t0 = lo + ti * T;
-      const Raw cur = load_raw(t0, load_ids(t0));
-      compute(cur, t0);
-    }
+  // ---- the key loop: this wave's 32-key blocks w, w + 4, ... of the split,
+  // NS - 1 blocks in flight ahead of the one being computed. Page ids are read
+  // two blocks before their loads are issued (two alternating sets, so no
+  // copy forces an early wait on a scalar load).
+  const int nblk = hi > lo ? (hi - lo + 31) / 32 : 0;
+  const int mine = nblk > w ? (nblk - 1 - w) / 4 + 1 : 0;
+  auto t0_of = [&](int j) __attribute__((always_inline)) { return lo + (w + 4 * j) * 32; };
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
+  Ids ids_a{0, 0}, ids_b{0, 0};
+  if (NS - 1 < mine) ids_a = load_ids(t0_of(NS - 1));
+  if (NS < mine) ids_b = load_ids(t0_of(NS));
+  auto step = [&](int j, Ids& ids) __attribute__((always_inline)) {
+    const int jn = j + NS - 1;
+    if (jn < mine) issue(t0_of(jn), ids, jn % NS);
+    const int later = (mine - 1 - j) < (NS - 1) ? (mine - 1 - j) : (NS - 1);
+    if (later >= 3) wait_vm<3 * NI>();
+    else if (later == 2) wait_vm<2 * NI>();
+    else if (later == 1) wait_vm<NI>();
+    else wait_vm<0>();
+    compute(t0_of(j), j % NS);
+    if (jn + 2 < mine) ids = load_ids(t0_of(jn + 2));
+  };
+  for (int j = 0; j < mine; j += 2) {
+    step(j, ids_a);
+    if (j + 1 < mine) step(j + 1, ids_b);
   }
 
   // ---- merge the four waves' states through LDS (wave order) -------------------
@@ -468,7 +611,7 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
       ml_s[w][rb * 32 + i32][1] = lrow[rb];
     }
   }
-  __syncthreads();
+  __syncthreads();                                 // every wave is past its key loop
   float wgt[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -552,7 +695,9 @@ int launch_d(const Params& p, int nrb, void* stream, int64_t grid) {
   switch (p.D) {
     case 64: return nrb == 2 ? launch_v<KT, 64, 2>(p, stream, grid) : launch_v<KT, 64, 1>(p, stream, grid);
     case 128: return nrb == 2 ? launch_v<KT, 128, 2>(p, stream, grid) : launch_v<KT, 128, 1>(p, stream, grid);
-    case 256: return launch_v<KT, 256, 1>(p, stream, grid);
+    case 256:
+      if constexpr (Storage<KT>::bytes == 1) return launch_v<KT, 256, 1>(p, stream, grid);
+      return SKV_ERR_UNSUPPORTED;
   }
   return SKV_ERR_SHAPE;
 }
@@ -563,6 +708,9 @@ bool mfma_supported(const Params& p) {
   if (p.q_dtype != SKV_BF16) return false;
   if (p.kv_dtype != SKV_BF16 && p.kv_dtype != SKV_INT8 && p.kv_dtype != SKV_FP8_E4M3) return false;
   if (p.D != 64 && p.D != 128 && p.D != 256) return false;
+  // a 32-key block of bf16 rows at D = 256 is 32 KiB of K and V: too big for the
+  // per-wave LDS ring, so that shape stays on the vector kernel
+  if (p.D == 256 && p.kv_dtype == SKV_BF16) return false;
   if (p.paged) return p.block_size >= 16;
   return p.kv_cap % 16 == 0;
 }
