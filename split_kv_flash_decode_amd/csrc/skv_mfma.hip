@@ -9,19 +9,27 @@
 // FP32 scales, page sizes 16 and 128, plain and transposed V).
 //
 // gfx950 design
-//  * One 256-thread workgroup per (work item, KV head, group of 32*NRB query
-//    rows). Its four waves take interleaved 32*TB-key tiles of the item's key
-//    range and each keeps its own online-softmax state for all of the group's
-//    rows; the four states are merged through LDS at the end, in wave order.
-//  * Every query row of a KV head (R * Hq / Hkv rows: GQA heads times MTP or
-//    verify rows) shares each key and value a wave loads, so a tile is a
+//  * One workgroup per (work item, KV head, group of up to 64 query rows).
+//    Every query row of a KV head (R * Hq / Hkv rows: GQA heads times MTP or
+//    verify rows) shares each key and value loaded, so a block of 32 keys is a
 //    dense contraction: S^T = K Q^T and O^T += V^T P^T run on
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-//  * K and V go straight from HBM to registers with 16-byte loads; no LDS
-//    staging, since no other wave reads them. Key order inside a 32-key block
-//    is permuted (tau) so that the S^T output a lane holds is 16 consecutive
-//    keys of one query row: exactly the P^T operand the P.V product needs and,
-//    for transposed V, exactly 16 contiguous bytes of a V^T row (one load).
+//  * Four key streams take interleaved 32-key blocks of the item's key range.
+//    With more than 32 rows, each stream has two waves (rows 0-31 and 32-63),
+//    eight waves in all, two per SIMD: one wave's vector work then fills the
+//    issue slots around the other's matrix-core and memory work. Each wave
+//    keeps the online-softmax state of its 32 rows for its stream; the four
+//    streams' states are merged through LDS at the end, in stream order.
+//  * K, V and the per-token scales go from HBM straight into a per-stream LDS
+//    ring (global_load_lds, NS stages, NS - 1 blocks in flight). Of the two
+//    waves of a stream one issues the K and scale loads, the other the V
+//    loads; one workgroup barrier per block step publishes the block and
+//    frees the stage being refilled.
+//  * Key order inside a 32-key block is permuted (tau) so that the S^T output
+//    a lane holds is 16 consecutive keys of one query row: exactly the P^T
+//    operand of the P.V product. Plain-layout V reaches the V^T operand through
+//    gfx950's transposing LDS reads (8 keys of one d per lane), from rows whose
+//    16-byte chunks the loads permute to keep those reads conflict-free.
 //  * FP8 codes become BF16 with v_cvt_scalef32_pk_bf16_fp8 and INT8 codes via
 //    fp32, both exactly; the per-token K scale multiplies the logits and the
 //    per-token V scale the probabilities, so the only rounding besides fp32
@@ -29,10 +37,11 @@
 //  * The softmax is online with lazy rescaling: the running maximum of a row
 //    is only raised (and acc, l rescaled) when a logit exceeds it by more than
 //    2^8, which a wave vote detects; the row max needs one cross-half shuffle.
-//  * Tiles that lie wholly inside the split and inside every row's visible
-//    range skip all masking; boundary tiles mask logits with selects (never
+//  * Blocks that lie wholly inside the split and inside every row's visible
+//    range skip all masking; boundary blocks mask logits with selects (never
 //    multiply-by-zero, so NaN-poisoned cache slots past a request's context
-//    never reach an accumulator) and zero V bytes of keys past the split.
+//    never reach an accumulator) and zero V codes and scales of keys past the
+//    split.
 
 #include <type_traits>
 
@@ -41,6 +50,9 @@
 namespace skv {
 
 namespace {
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // MFMA row i of the K operand of a 32-key block holds key tau(i); then output
 // value v of a lane in wave half h is key 16 h + v.
@@ -59,21 +71,6 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, uint32_t w2, ui
     r = u32x4{w0, w1, w2, w3};
   }
   return __builtin_bit_cast(bf16x8, r);
-}
-
-// Element c of a token's V chunk (plain layout) for two tokens -> packed bf16
-// pair (token0 in the low half).
-template <class KT>
-__device__ __forceinline__ uint32_t vpair(uint32_t t0, uint32_t t1, int c) {
-  if constexpr (__is_same(KT, FP8)) {
-    const uint32_t sel = (uint32_t)(c & 3) | ((uint32_t)(4 + (c & 3)) << 8) | 0x0C0C0000u;
-    return fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(t1, t0, sel));
-  } else if constexpr (__is_same(KT, I8)) {
-    return pack_bf16x2(i8_to_f32(t0, c & 3), i8_to_f32(t1, c & 3));
-  } else {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    return __builtin_amdgcn_perm(t1, t0, sel);
-  }
 }
 
 __device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
@@ -128,16 +125,15 @@ __device__ __forceinline__ int cload(const int* p) {
   return *(const __attribute__((address_space(4))) int*)p;
 }
 
-template <class KT, int D, int NRB, bool VT>
-__global__ __launch_bounds__(256) void partial_mfma(Params p) {
+template <class KT, int D, int NRH, bool VT>
+__global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int EB = Storage<KT>::bytes;
   constexpr bool QUANT = Storage<KT>::quant;
-  constexpr int KS = D / 16;                     // Q.K^T k-steps of 16 d
   constexpr int DB = D / 32;                     // P.V d-blocks of 32
-  constexpr int ROWS = 32 * NRB;
+  constexpr int NT = 256 * NRH;                  // threads: 4 key streams x NRH row halves
+  constexpr int ROWS = 32 * NRH;
   constexpr int RB = D * EB;                     // bytes of one key row
-  constexpr int NCH = RB / 32;                   // 1 KiB load chunks of K (and of V) per 32-key block
-  constexpr int NI = 2 * NCH + (QUANT ? 1 : 0);  // direct-to-LDS loads per block
+  constexpr int NCH = RB / 32;                   // 16-byte K chunks per lane and block
   // Stage: K rows (32 RB bytes), V (plain: two 16-key groups of rows, the
   // second shifted by 128 bytes so the two lane halves read different LDS
   // banks; transposed: 16-byte key runs of V^T rows), then 32 K and 32 V
@@ -153,12 +149,29 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
   constexpr int QBYTES = ROWS * QS * 2;
   constexpr int BUDGET = 156 * 1024;
   constexpr int NS0 = (BUDGET - QBYTES) / (4 * STAGE);
-  constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per wave
+  constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per key stream
   constexpr int RING = 4 * NS * STAGE;
   constexpr int PD = D + 1;                      // merge buffer row stride (floats)
   constexpr int MERGE = ROWS * PD * 4;
   constexpr int SMEM0 = RING > MERGE ? RING : MERGE;
-  constexpr int VB = (D / 32) * EB;              // plain V: bytes of a lane's d chunk per key
+  // Plain V rows sit in LDS with their 16-byte chunks permuted, chunk c of
+  // row r (key r of a 16-key group) at c ^ vswz(r), so that the transposing
+  // LDS reads of the P.V operand (8 keys of one d per lane for 8-bit codes,
+  // 4 for bf16) hit distinct banks across a half-wave. Rows of one 256-byte
+  // bank line (KPR of them) share their banks; the XOR separates the keys
+  // that would collide.
+  constexpr int NCK = RB / 16;                   // 16-byte chunks per key row
+  constexpr int KPR = RB >= 256 ? 1 : 256 / RB;  // key rows per 256-byte bank line
+  constexpr int SPAN = EB == 1 ? 2 : 4;          // chunks per key one half-wave reads
+  auto vswz = [](int r) __attribute__((always_inline)) {
+    return SPAN * ((r / KPR) % (NCK / SPAN));
+  };
+  // Direct-to-LDS loads per block: K, V and (quantized) one of scales. With
+  // two row halves the first half's wave of a stream issues K and the
+  // scales, the second half's wave V.
+  constexpr int NVL = VT ? U / 2 : KIG;          // V loads per 16-key group
+  constexpr int NK = 2 * KIG + (QUANT ? 1 : 0);
+  constexpr int NV = 2 * NVL;
 
   __shared__ __attribute__((aligned(16))) char smem[SMEM0 + QBYTES];
   __shared__ float ml_s[4][ROWS][2];
@@ -168,10 +181,12 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sid = w & 3;                         // key stream
+  const int rh = w >> 2;                         // row half
   const int lane = tid & 63;
   const int i32 = lane & 31;
   const int hh = lane >> 5;
-  char* ring = smem + w * NS * STAGE;
+  char* ring = smem + sid * NS * STAGE;
 
   int blk = blockIdx.x;
   const int rg = blk % p.row_groups;
@@ -189,8 +204,8 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
 
   // Query rows of the group -> LDS (bf16, rows padded by 16 bytes); rows past
   // rho are zero. The B operand of S^T = K Q^T is read back per k-step:
-  // lane holds row i32 of a row block, d in [hh * D/2 + 8 kk, +8).
-  for (int idx = tid; idx < ROWS * (D / 8); idx += 256) {
+  // lane holds row i32 of the wave's rows, d in [hh * D/2 + 8 kk, +8).
+  for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
     const int row = idx / (D / 8), c8 = idx - row * (D / 8);
     const int r = rbase + row;
     u32x4 x = {0u, 0u, 0u, 0u};
@@ -201,36 +216,30 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
     }
     *reinterpret_cast<u32x4*>(&q_s[row * QS + 8 * c8]) = x;
   }
-  int vlo[NRB], vhi[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int r = rbase + rb * 32 + i32;
-    vlo[rb] = 0;
-    vhi[rb] = 0;
-    if (r < p.rho) row_range(ctx, p.R, p.causal, p.window, r / p.G, &vlo[rb], &vhi[rb]);
-  }
-  // Keys every row of the group sees: [ilo, ihi).
-  int ilo, ihi;
-  {
+  // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
+  const int wrow0 = rbase + 32 * rh;
+  int vlo = 0, vhi = 0;
+  if (wrow0 + i32 < p.rho) row_range(ctx, p.R, p.causal, p.window, (wrow0 + i32) / p.G, &vlo, &vhi);
+  // Keys every row of the wave sees: [ilo, ihi) (empty for a wave past rho).
+  int ilo = 0, ihi = 0;
+  if (wrow0 < p.rho) {
+    const int last = (wrow0 + 31 < p.rho ? wrow0 + 31 : p.rho - 1);
     int a0, a1, c0, c1;
-    row_range(ctx, p.R, p.causal, p.window, rbase / p.G, &a0, &a1);
-    row_range(ctx, p.R, p.causal, p.window, (rbase + nrow - 1) / p.G, &c0, &c1);
-    ilo = __builtin_amdgcn_readfirstlane(a0 > c0 ? a0 : c0);
-    ihi = __builtin_amdgcn_readfirstlane(a1 < c1 ? a1 : c1);
+    row_range(ctx, p.R, p.causal, p.window, wrow0 / p.G, &a0, &a1);
+    row_range(ctx, p.R, p.causal, p.window, last / p.G, &c0, &c1);
+    ilo = a0 > c0 ? a0 : c0;
+    ihi = a1 < c1 ? a1 : c1;
   }
+  ilo = __builtin_amdgcn_readfirstlane(ilo);
+  ihi = __builtin_amdgcn_readfirstlane(ihi);
   __syncthreads();
 
-  floatx16 acc[NRB][DB];
-  float mrun[NRB], lrun[NRB];
+  floatx16 acc[DB];
+  float mrun = -INFINITY, lrun = 0.0f;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    mrun[rb] = -INFINITY;
-    lrun[rb] = 0.0f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][db][v] = 0.0f;
-  }
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
 
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
@@ -284,7 +293,6 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
 #pragma unroll
     for (int n = 0; n < KIG; ++n)
       koffs[gp][n] = (uint32_t)(((lane & 15) ^ (8 * gp)) * RB + (4 * n + (lane >> 4)) * 16);
-  constexpr int NVL = VT ? U / 2 : KIG;          // V loads per group
   uint32_t voffs[NVL];
   {
     const int dstride = (p.paged ? (1 << p.bs_shift) : p.kv_cap) * EB;
@@ -294,42 +302,65 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
         const int u = 2 * n + (lane >> 5);
         voffs[n] = (uint32_t)((32 * (u / EB) + i32) * dstride + (u % EB) * 16);
       } else {
+        // LDS slot (row, chunk c) of the group receives global chunk
+        // c ^ vswz(row) of that row
         constexpr int LPR = RB / 16;
-        voffs[n] = (uint32_t)((n * (1024 / RB) + lane / LPR) * RB + (lane % LPR) * 16);
+        const int row = n * (1024 / RB) + lane / LPR;
+        voffs[n] = (uint32_t)(row * RB + ((lane % LPR) ^ vswz(row)) * 16);
       }
     }
   }
 
-  // Issue the direct-to-LDS loads of the 32-key block at t0 into stage st.
+  // Issue this wave's share of the direct-to-LDS loads of the block at t0
+  // into stage st: K and the scales (first row half), V (second row half),
+  // or all of them (one row half).
   auto issue = [&](int t0, const Ids& id, int st) __attribute__((always_inline)) {
     const uint32_t S = lds_addr(ring + st * STAGE);
     const int64_t R0 = grp_row(id, t0, 0), R1 = grp_row(id, t0, 1);
-#pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-      const char* kb = kbase + (gp ? R1 : R0) * RB;
-#pragma unroll
-      for (int n = 0; n < KIG; ++n) dma16s(kb, koffs[gp][n], S + (gp * KIG + n) * 1024);
-    }
-    if constexpr (VT) {
+    if (NRH == 1 || rh == 0) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        const char* vb = vbase + grp_vt(id, t0, gp) * EB;
+        const char* kb = kbase + (gp ? R1 : R0) * RB;
 #pragma unroll
-        for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + (gp * NVL + n) * 1024);
+        for (int n = 0; n < KIG; ++n) dma16s(kb, koffs[gp][n], S + (gp * KIG + n) * 1024);
       }
+      if constexpr (QUANT) {
+        // lane l < 32: K scale of key l; l >= 32: V scale of key l - 32
+        const int k = i32;
+        const int64_t r = ((k >= 16) ? R1 : R0) + (k & 15);
+        dma4((hh ? p.vs : p.ks) + r, S + KSZ + VSZ);
+      }
+    }
+    if (NRH == 1 || rh == 1) {
+      if constexpr (VT) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const char* vb = vbase + grp_vt(id, t0, gp) * EB;
+#pragma unroll
+          for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + (gp * NVL + n) * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const char* vb = vbase + (gp ? R1 : R0) * RB;
+#pragma unroll
+          for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + gp * VGS + n * 1024);
+        }
+      }
+    }
+  };
+  // Wait until at most `blocks` of this wave's later blocks are in flight.
+  auto wait_own = [&](int blocks) __attribute__((always_inline)) {
+    constexpr int A = NRH == 1 ? NK + NV : NK;   // loads per block of a first-half wave
+    constexpr int B = NRH == 1 ? NK + NV : NV;   // ... of a second-half wave
+    if (rh == 0) {
+      if (blocks >= 2) wait_vm<2 * A>();
+      else if (blocks == 1) wait_vm<A>();
+      else wait_vm<0>();
     } else {
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        const char* vb = vbase + (gp ? R1 : R0) * RB;
-#pragma unroll
-        for (int n = 0; n < NVL; ++n) dma16s(vb, voffs[n], S + KSZ + gp * VGS + n * 1024);
-      }
-    }
-    if constexpr (QUANT) {
-      // lane l < 32: K scale of key l; l >= 32: V scale of key l - 32
-      const int k = i32;
-      const int64_t r = ((k >= 16) ? R1 : R0) + (k & 15);
-      dma4((hh ? p.vs : p.ks) + r, S + KSZ + VSZ);
+      if (blocks >= 2) wait_vm<2 * B>();
+      else if (blocks == 1) wait_vm<B>();
+      else wait_vm<0>();
     }
   };
 
@@ -337,110 +368,23 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
   // position (tau % 16) ^ (8 group); its 16-byte chunk j of the row is at
   // + j * 256.
   const int kread = ((tau(i32) >> 4) * KIG) * 1024 + ((tau(i32) & 15) ^ (8 * (tau(i32) >> 4))) * 16;
+  // B operand of S^T = K Q^T, read from LDS at every block: k-step kk of lane
+  // (i32, hh) is row 32 rh + i32, d in [hh D/2 + 8 kk, +8).
+  const int qoff0 = (32 * rh + i32) * QS + hh * (D / 2);
 
-  // Logits of one 32-key block: t = s * c - mu, with c = scale * log2(e) *
-  // k_scale and mu the running reference maximum, so that the probability is
-  // exp2(t). MASK selects the boundary version (causal / window / split end by
-  // select, never by multiplying with zero). Returns whether a row's reference
-  // must rise (a logit more than 2^8 above it).
-  auto logits = [&](auto mask_tag, floatx16 (&s)[NRB], const float (&c)[16], int t0, int kb,
-                    float (&mloc)[NRB]) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float mu = (mrun[rb] == -INFINITY) ? 0.0f : mrun[rb];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float t = __builtin_fmaf(s[rb][v], c[v], -mu);
-        if constexpr (MASK) {
-          const int k = t0 + kb + v;
-          const bool vis = (k < hi) & (k >= vlo[rb]) & (k < vhi[rb]);
-          t = vis ? t : -INFINITY;
-        }
-        s[rb][v] = t;
-        mx = fmaxf(mx, t);
-      }
-      mloc[rb] = mx;
-      need |= (mrun[rb] == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
-    }
-    return need;
-  };
-  // Probabilities times the V scale as the bf16 P^T operand; l accumulates.
-  auto probs = [&](auto mask_tag, const floatx16 (&s)[NRB], const float (&sv)[16],
-                   bf16x8 (&pf)[NRB][2]) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      float lsum = 0.0f;
-      float pv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pe = fexp2(s[rb][v]);
-        lsum += pe;
-        if constexpr (QUANT) {
-          if constexpr (MASK) {
-            pv[v] = pe > 0.0f ? pe * sv[v] : 0.0f;    // NaN scales of masked keys stay out
-          } else {
-            pv[v] = pe * sv[v];
-          }
-        } else {
-          pv[v] = pe;
-        }
-      }
-      lrun[rb] += lsum;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const u32x4 pk = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
-                          pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]), pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
-        pf[rb][kh] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-  };
-  // Raise the references of rows whose logits exceeded them (rare: the wave
-  // votes first); alpha = 1 and shift = 0 leave the other rows unchanged.
-  auto rescale = [&](floatx16 (&s)[NRB], const float (&mloc)[NRB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float mu = (mrun[rb] == -INFINITY) ? 0.0f : mrun[rb];
-      const float mt = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 32, 64));   // row max - mu
-      const float mnew = fmaxf(mrun[rb], mt + mu);
-      const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun[rb] - mnew);   // 0 when mrun = -inf
-      const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
-      lrun[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[rb][db][v] *= alpha;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[rb][v] -= shift;
-      mrun[rb] = mnew;
-    }
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
-  };
-
-  auto compute = [&](int t0, int st) __attribute__((always_inline)) {
+  // ---- one 32-key block in stage st ------------------------------------------
+  // Blocks wholly inside the split and inside every row's visible range skip
+  // all masking; on the others (a wave-uniform test) small branches mask
+  // logits, V scales and V codes. The matrix-core code is shared by both
+  // kinds, so the accumulators keep one register assignment.
+  auto compute = [&](int t0, int st, auto&& mid) __attribute__((always_inline)) {
     const char* S = ring + st * STAGE;
-    const bool interior =
-        __builtin_amdgcn_readfirstlane((int)((t0 + 32 <= hi) && (t0 >= ilo) && (t0 + 32 <= ihi))) != 0;
+    const bool boundary =
+        __builtin_amdgcn_readfirstlane((int)((t0 + 32 > hi) | (t0 < ilo) | (t0 + 32 > ihi))) != 0;
     const int kb = 16 * hh;                       // first key of this lane's 16
-    // ---- S^T = K Q^T for this 32-key block
-    floatx16 s[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[rb][v] = 0.0f;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(s[rb]));
-    int qoff = i32 * QS + hh * (D / 2);
+    // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
+    floatx16 s;
+    int qoff = qoff0;
     asm volatile("" : "+v"(qoff));                // re-read Q from LDS every block
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -455,16 +399,11 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
         } else {
           kf = cvt8<KT>(kc[0], kc[1], kc[2], kc[3]);
         }
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff + rb * 32 * QS + 8 * kk]));
-          s[rb] = mfma(kf, qf, s[rb]);
-        }
+        const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff + 8 * kk]));
+        s = mfma(kf, qf, kk == 0 ? floatx16{} : s);
       }
     }
-    // S feeds VALU code: keep it in VGPRs (the MFMA writes them directly).
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) asm volatile("" : "+v"(s[rb]));
+    mid();                                        // e.g. the next block's loads
     // ---- per-key scales (K scale folded into c, V scale into the probabilities)
     float c[16], sv[16];
     if constexpr (QUANT) {
@@ -486,17 +425,75 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
         sv[v] = 1.0f;
       }
     }
-    float mloc[NRB];
-    const bool need = interior ? logits(std::false_type{}, s, c, t0, kb, mloc)
-                               : logits(std::true_type{}, s, c, t0, kb, mloc);
-    if (__any(need)) rescale(s, mloc);
-    bf16x8 pf[NRB][2];
-    if (interior)
-      probs(std::false_type{}, s, sv, pf);
-    else
-      probs(std::true_type{}, s, sv, pf);
-    // ---- O^T += V^T P^T
     const int nv = hi - (t0 + kb);                // keys of this lane's 16 inside the split
+    if (boundary) {
+      // the V scales of keys past the split may be NaN: zero them, so masked
+      // keys give exactly zero (the empty asm keeps this a branch)
+      int n = nv;
+      asm volatile("" : "+v"(n));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = (v < n) ? sv[v] : 0.0f;
+    }
+    // ---- logits t = s * c - mu (mu: the running reference maximum), so that
+    // the probability is exp2(t); boundary blocks then replace masked logits
+    // by -inf with selects (never by multiplying with zero)
+    const float mu = (mrun == -INFINITY) ? 0.0f : mrun;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = __builtin_fmaf(s[v], c[v], -mu);
+    if (boundary) {
+      asm volatile("");
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int k = t0 + kb + v;
+        const bool vis = (k < hi) & (k >= vlo) & (k < vhi);
+        s[v] = vis ? s[v] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    // ---- lazy rescale: the reference only rises when a logit exceeds it by
+    // more than 2^8 (rare; the wave votes first)
+    const bool need = (mrun == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+    if (__any(need)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
+      const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
+      const float mnew = fmaxf(mrun, mt + mu);
+      const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
+      const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
+      lrun *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] -= shift;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
+    }
+    // ---- probabilities times the V scale as the bf16 P^T operand
+    bf16x8 pf[2];
+    {
+      float lsum = 0.0f;
+      float pv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pe = fexp2(s[v]);
+        lsum += pe;
+        pv[v] = QUANT ? pe * sv[v] : pe;
+      }
+      lrun += lsum;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const u32x4 pk = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
+                          pack_bf16x2(pv[8 * kh + 4], pv[8 * kh + 5]), pack_bf16x2(pv[8 * kh + 6], pv[8 * kh + 7])};
+        pf[kh] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+    // ---- O^T += V^T P^T (V codes of keys past the split zeroed on boundary
+    // blocks: they may be NaN-poisoned)
     if constexpr (VT) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -507,7 +504,8 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[4 * e + q] = vc[q];
         }
-        if (!interior) {
+        if (boundary) {
+          asm volatile("");
 #pragma unroll
           for (int q = 0; q < 4 * EB; ++q) x[q] = keep_bytes(x[q], q * (4 / EB), nv, 4 / EB);
         }
@@ -519,134 +517,135 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
           } else {
             vf = cvt8<KT>(x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]);
           }
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) acc[rb][db] = mfma(vf, pf[rb][kh], acc[rb][db]);
+          acc[db] = mfma(vf, pf[kh], acc[db]);
         }
       }
     } else {
-      constexpr int VPW = VB >= 4 ? VB / 4 : 1;
-      uint32_t vr[16][VPW];
-      const char* vrow = S + KSZ + hh * VGS + VB * i32;
+      // transposing LDS reads: in each 16-lane group (wave half hh, d half mh
+      // of a 32-d block), lane i gets 8 (8-bit) or 4 (bf16) consecutive keys
+      // of d = 32 db + 16 mh + i; lane r of the group supplies the address of
+      // the row segment that the transpose distributes (key 2 j + r / 2 ...)
+      const int gi = lane & 15;
+      const int mh = (lane >> 4) & 1;
+      const char* vg = S + KSZ + hh * VGS;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const char* src = vrow + e * RB;
-        if constexpr (VB == 2) {
-          vr[e][0] = *reinterpret_cast<const uint16_t*>(src);
-        } else if constexpr (VB == 4) {
-          vr[e][0] = *reinterpret_cast<const uint32_t*>(src);
-        } else if constexpr (VB == 8) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-          vr[e][0] = x[0];
-          vr[e][1] = x[1];
-        } else {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) vr[e][q] = x[q];
-        }
-      }
-      if (!interior) {                            // keys past the split may be NaN-poisoned
+        for (int kh = 0; kh < 2; ++kh) {
+          uint32_t x[4];
+          if constexpr (EB == 1) {
+            const int key = 8 * kh + (gi >> 1);
+            const int c = 2 * db + mh;
+            const char* a8 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
+            const v2i32 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i32*)(a8));
+            x[0] = (uint32_t)t[0];
+            x[1] = (uint32_t)t[1];
+            x[2] = x[3] = 0u;
+          } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
+            for (int q = 0; q < 2; ++q) {
+              const int key = 8 * kh + 4 * q + (gi >> 2);
+              const int c = 4 * db + 2 * mh + ((gi & 3) >> 1);
+              const char* a16 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
+              const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4i16*)(a16));
+              const u32x2 u = __builtin_bit_cast(u32x2, t);
+              x[2 * q] = u[0];
+              x[2 * q + 1] = u[1];
+            }
+          }
+          if (boundary) {
+            asm volatile("");
+            constexpr int PW = 4 / EB;                 // keys per word
 #pragma unroll
-          for (int q = 0; q < VPW; ++q) vr[e][q] = (e < nv) ? vr[e][q] : 0u;
-      }
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int wi = (EB == 1) ? (db >> 2) : (db >> 1);
-          u32x4 rr;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) rr[u] = vpair<KT>(vr[8 * kh + 2 * u][wi], vr[8 * kh + 2 * u + 1][wi], db);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, rr);
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) acc[rb][db] = mfma(vf, pf[rb][kh], acc[rb][db]);
+            for (int q = 0; q < 2 * EB; ++q) x[q] = keep_bytes(x[q], 8 * kh + q * PW, nv, PW);
+          }
+          acc[db] = mfma(cvt8<KT>(x[0], x[1], x[2], x[3]), pf[kh], acc[db]);
         }
       }
     }
     // The accumulators only meet VALU code in the rare rescale and at the
     // end: keep them in AGPRs across blocks.
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[rb][db]));
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
   };
 
-  // ---- the key loop: this wave's 32-key blocks w, w + 4, ... of the split,
-  // NS - 1 blocks in flight ahead of the one being computed. Page ids are read
-  // two blocks before their loads are issued (two alternating sets, so no
-  // copy forces an early wait on a scalar load).
+  // ---- the key loop ----------------------------------------------------------
+  // Key stream sid takes the split's 32-key blocks sid, sid + 4, ...; both
+  // row halves of a stream consume every block of it. All waves step
+  // together, one workgroup barrier per step (the same number of steps for
+  // every wave): at step j the barrier publishes block j (each wave waited
+  // for its own loads of it) and frees the stage of block j - 1, into which
+  // block j + NS - 1 is then loaded.
   const int nblk = hi > lo ? (hi - lo + 31) / 32 : 0;
-  const int mine = nblk > w ? (nblk - 1 - w) / 4 + 1 : 0;
-  auto t0_of = [&](int j) __attribute__((always_inline)) { return lo + (w + 4 * j) * 32; };
+  const int mine = nblk > sid ? (nblk - 1 - sid) / 4 + 1 : 0;
+  const int steps = (nblk + 3) / 4;
+  auto t0_of = [&](int j) __attribute__((always_inline)) { return lo + (sid + 4 * j) * 32; };
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
-  Ids ids_a{0, 0}, ids_b{0, 0};
-  if (NS - 1 < mine) ids_a = load_ids(t0_of(NS - 1));
-  if (NS < mine) ids_b = load_ids(t0_of(NS));
-  auto step = [&](int j, Ids& ids) __attribute__((always_inline)) {
+  // page ids of the block issued at the next step, read one step ahead
+  Ids ids{0, 0};
+  if (NS - 1 < mine) ids = load_ids(t0_of(NS - 1));
+  for (int j = 0; j < steps; ++j) {
+    {
+      const int r = mine - 1 - j;                 // own blocks issued after block j: min(r, NS - 2)
+      wait_own(r < NS - 2 ? r : NS - 2);
+    }
+    __syncthreads();
     const int jn = j + NS - 1;
-    if (jn < mine) issue(t0_of(jn), ids, jn % NS);
-    const int later = (mine - 1 - j) < (NS - 1) ? (mine - 1 - j) : (NS - 1);
-    if (later >= 3) wait_vm<3 * NI>();
-    else if (later == 2) wait_vm<2 * NI>();
-    else if (later == 1) wait_vm<NI>();
-    else wait_vm<0>();
-    compute(t0_of(j), j % NS);
-    if (jn + 2 < mine) ids = load_ids(t0_of(jn + 2));
-  };
-  for (int j = 0; j < mine; j += 2) {
-    step(j, ids_a);
-    if (j + 1 < mine) step(j + 1, ids_b);
+    // the loads of block jn go out between the two matrix-core phases of
+    // block j, so that the eight waves do not all queue on the vector memory
+    // unit right after the barrier
+    auto next_loads = [&]() __attribute__((always_inline)) {
+      if (jn < mine) issue(t0_of(jn), ids, jn % NS);
+    };
+    if (j < mine)
+      compute(t0_of(j), j % NS, next_loads);
+    else
+      next_loads();
+    if (jn + 1 < mine) ids = load_ids(t0_of(jn + 1));
   }
 
-  // ---- merge the four waves' states through LDS (wave order) -------------------
-  float lrow[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    lrow[rb] = lrun[rb] + __shfl_xor(lrun[rb], 32, 64);
-    if (hh == 0) {
-      ml_s[w][rb * 32 + i32][0] = mrun[rb];
-      ml_s[w][rb * 32 + i32][1] = lrow[rb];
-    }
+  // ---- merge the four streams' states through LDS (stream order) ------------
+  const int row = 32 * rh + i32;                  // this lane's row within the group
+  const float lrow = lrun + __shfl_xor(lrun, 32, 64);
+  if (hh == 0) {
+    ml_s[sid][row][0] = mrun;
+    ml_s[sid][row][1] = lrow;
   }
   __syncthreads();                                 // every wave is past its key loop
-  float wgt[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    const int row = rb * 32 + i32;
+  float wgt;
+  {
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
-      if (ml_s[ww][row][1] > 0.0f) M = fmaxf(M, ml_s[ww][row][0]);
-    wgt[rb] = lrow[rb] > 0.0f ? fexp2(mrun[rb] - M) : 0.0f;
-    if (w == 0 && hh == 0) {
+    for (int ss = 0; ss < 4; ++ss)
+      if (ml_s[ss][row][1] > 0.0f) M = fmaxf(M, ml_s[ss][row][0]);
+    wgt = lrow > 0.0f ? fexp2(mrun - M) : 0.0f;
+    if (sid == 0 && hh == 0) {
       float L = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float lw = ml_s[ww][row][1];
-        if (lw > 0.0f) L += fexp2(ml_s[ww][row][0] - M) * lw;
+      for (int ss = 0; ss < 4; ++ss) {
+        const float lw = ml_s[ss][row][1];
+        if (lw > 0.0f) L += fexp2(ml_s[ss][row][0] - M) * lw;
       }
       fin_s[row][0] = M;
       fin_s[row][1] = L;
     }
   }
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  for (int ss = 0; ss < 4; ++ss) {
+    if (sid == ss) {
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int di = 8 * (v >> 2) + 4 * hh + (v & 3);
-            const int d = VT ? 32 * db + di : (D / 32) * di + db;
-            const int idx = (rb * 32 + i32) * PD + d;
-            const float val = wgt[rb] * acc[rb][db][v];
-            acc_s[idx] = (ww == 0) ? val : acc_s[idx] + val;
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int di = 8 * (v >> 2) + 4 * hh + (v & 3);
+          const int d = 32 * db + di;
+          const int idx = row * PD + d;
+          const float val = wgt * acc[db][v];
+          acc_s[idx] = (ss == 0) ? val : acc_s[idx] + val;
         }
       }
     }
@@ -654,24 +653,24 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
   }
 
   if (p.finalize) {
-    for (int idx = tid; idx < nrow * D; idx += 256) {
-      const int row = idx / D, d = idx - (idx / D) * D;
-      const int r = rbase + row;
+    for (int idx = tid; idx < nrow * D; idx += NT) {
+      const int rr = idx / D, d = idx - (idx / D) * D;
+      const int r = rbase + rr;
       int j, hq;
       row_jh(p, g, r, &j, &hq);
       const float s2 = p.has_sink ? p.sinks[hq] * kLog2e : 0.0f;
       store_o1(p, qo_idx(p, b, j, hq, d),
-               finalize_one(fin_s[row][0], fin_s[row][1], acc_s[row * PD + d], p.has_sink, s2));
+               finalize_one(fin_s[rr][0], fin_s[rr][1], acc_s[rr * PD + d], p.has_sink, s2));
     }
   } else {
     const int64_t slot = (int64_t)it.slot_item * p.Hkv + g;
-    for (int idx = tid; idx < nrow * D; idx += 256) {
-      const int row = idx / D, d = idx - (idx / D) * D;
-      const int64_t rec = slot * p.rho + rbase + row;
-      p.pacc[rec * D + d] = acc_s[row * PD + d];
+    for (int idx = tid; idx < nrow * D; idx += NT) {
+      const int rr = idx / D, d = idx - (idx / D) * D;
+      const int64_t rec = slot * p.rho + rbase + rr;
+      p.pacc[rec * D + d] = acc_s[rr * PD + d];
       if (d == 0) {
-        p.pm[rec] = fin_s[row][0];
-        p.pl[rec] = fin_s[row][1];
+        p.pm[rec] = fin_s[rr][0];
+        p.pl[rec] = fin_s[rr][1];
       }
     }
   }
@@ -679,22 +678,22 @@ __global__ __launch_bounds__(256) void partial_mfma(Params p) {
 
 namespace {
 
-template <class KT, int D, int NRB>
+template <class KT, int D, int NRH>
 int launch_v(const Params& p, void* stream, int64_t grid) {
   if (p.v_layout == SKV_V_TRANSPOSED)
-    hipLaunchKernelGGL((partial_mfma<KT, D, NRB, true>), dim3((unsigned)grid), dim3(256), 0,
+    hipLaunchKernelGGL((partial_mfma<KT, D, NRH, true>), dim3((unsigned)grid), dim3(256 * NRH), 0,
                        (hipStream_t)stream, p);
   else
-    hipLaunchKernelGGL((partial_mfma<KT, D, NRB, false>), dim3((unsigned)grid), dim3(256), 0,
+    hipLaunchKernelGGL((partial_mfma<KT, D, NRH, false>), dim3((unsigned)grid), dim3(256 * NRH), 0,
                        (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ERR_LAUNCH;
 }
 
 template <class KT>
-int launch_d(const Params& p, int nrb, void* stream, int64_t grid) {
+int launch_d(const Params& p, int nrh, void* stream, int64_t grid) {
   switch (p.D) {
-    case 64: return nrb == 2 ? launch_v<KT, 64, 2>(p, stream, grid) : launch_v<KT, 64, 1>(p, stream, grid);
-    case 128: return nrb == 2 ? launch_v<KT, 128, 2>(p, stream, grid) : launch_v<KT, 128, 1>(p, stream, grid);
+    case 64: return nrh == 2 ? launch_v<KT, 64, 2>(p, stream, grid) : launch_v<KT, 64, 1>(p, stream, grid);
+    case 128: return nrh == 2 ? launch_v<KT, 128, 2>(p, stream, grid) : launch_v<KT, 128, 1>(p, stream, grid);
     case 256:
       if constexpr (Storage<KT>::bytes == 1) return launch_v<KT, 256, 1>(p, stream, grid);
       return SKV_ERR_UNSUPPORTED;
@@ -716,15 +715,17 @@ bool mfma_supported(const Params& p) {
 }
 
 int launch_partial_mfma(Params p, void* stream) {
-  const int nrb = (p.D == 256 || p.rho <= 32) ? 1 : 2;
-  const int rows = 32 * nrb;
+  // two row halves (eight waves, two per SIMD) when a KV head has more than
+  // 32 query rows; D = 256 keeps one (its accumulators need the registers)
+  const int nrh = (p.D == 256 || p.rho <= 32) ? 1 : 2;
+  const int rows = 32 * nrh;
   p.row_groups = (p.rho + rows - 1) / rows;
   const int64_t grid = (int64_t)p.n_items * p.Hkv * p.row_groups;
   if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
   switch (p.kv_dtype) {
-    case SKV_BF16: return launch_d<BF16>(p, nrb, stream, grid);
-    case SKV_INT8: return launch_d<I8>(p, nrb, stream, grid);
-    case SKV_FP8_E4M3: return launch_d<FP8>(p, nrb, stream, grid);
+    case SKV_BF16: return launch_d<BF16>(p, nrh, stream, grid);
+    case SKV_INT8: return launch_d<I8>(p, nrh, stream, grid);
+    case SKV_FP8_E4M3: return launch_d<FP8>(p, nrh, stream, grid);
   }
   return SKV_ERR_DTYPE;
 }
