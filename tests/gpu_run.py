@@ -48,3 +48,20 @@ def run(p, mode: str = "split", num_splits: int = 1, impl: str = "auto", ws_fill
 
 def to_f64(o: torch.Tensor):
     return o.detach().double().cpu().numpy()
+
+
+def bench_step(p, impl: str = "auto", ws_fill: Optional[float] = None):
+    """The step ``bench.py`` times: plan (host) -> metadata copy -> partial -> combine,
+    through splitkv_partial / splitkv_combine with the planner's capacity.
+    Returns (o, workspace, plan)."""
+    s = p.spec
+    d, a, o = desc_args(p, impl)
+    ph = skv.plan_hints(s.B, s.R, s.Hkv, causal=s.causal, window=s.window,
+                        partitions_per_request=s.partitions_per_request)
+    plan = skv.Plan(ph, list(s.ctx), p.device)
+    ws = skv.Workspace(d, plan.info.slots, p.device, fill=ws_fill)
+    plan.refresh(list(s.ctx))
+    skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
+    skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
+    torch.cuda.synchronize()
+    return o, ws, plan

@@ -1,0 +1,48 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration that
+``bench.py`` times (host plan -> metadata copy -> partial -> combine).
+
+The fp64 oracle checks whole requests one at a time: every request where the
+oracle is quick (configs 2 and 3), sampled requests otherwise (config 4: the
+first, a middle and the last of 200 requests of 200,000 keys; config 5: the
+200,000-key request and two 1,024-key ones). Each sampled request is copied to
+the host with only the pages its table row references. Same tolerance as the
+reduced-shape tests: |d| <= 5e-3 + 5e-3 |ref|, rel-L2 <= 1e-2, row cosine >=
+0.9999. Scratch records start NaN-filled, so a record the combine reads but no
+partial wrote shows up as NaN.
+"""
+
+from __future__ import annotations
+
+import gc
+
+import pytest
+import torch
+
+from skvgen import config_spec, extract_request, make_problem
+from tests.gpu_run import bench_step, to_f64
+from tests.helpers import compare, oracle_output
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {2: None, 3: None, 4: (0, 97, 199), 5: (0, 1, 15)}
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_full_size_bench_step_matches_oracle(n):
+    spec = config_spec(n)
+    print(f"[full cfg{n}] {spec.name}: B {spec.B}, keys {sum(spec.ctx)}", flush=True)
+    p = make_problem(spec, seed=4, device="cuda")
+    o, ws, plan = bench_step(p, ws_fill=float("nan"))
+    out = to_f64(o)
+    reqs = SAMPLES[n] or range(spec.B)
+    try:
+        for b in reqs:
+            sub = extract_request(p, b)
+            ref = oracle_output(sub)[0]
+            st = compare(out[b], ref, "lowp")
+            print(f"[full cfg{n} request {b} ctx {spec.ctx[b]}] {st}", flush=True)
+            assert st["ok"], (n, b, st)
+    finally:
+        del p, o, ws, plan
+        gc.collect()
+        torch.cuda.empty_cache()
