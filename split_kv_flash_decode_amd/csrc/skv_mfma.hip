@@ -21,10 +21,10 @@
 //    keeps the online-softmax state of its 32 rows for its stream; the four
 //    streams' states are merged through LDS at the end, in stream order.
 //  * K, V and the per-token scales go from HBM straight into a per-stream LDS
-//    ring (global_load_lds, NS stages, NS - 1 blocks in flight). Of the two
-//    waves of a stream one issues the K and scale loads, the other the V
-//    loads; one workgroup barrier per block step publishes the block and
-//    frees the stage being refilled.
+//    ring (global_load_lds of whole key rows, NS stages). Of the two waves of
+//    a stream one issues the K and scale loads, the other the V loads. With
+//    four stages one workgroup barrier per two blocks publishes them and
+//    frees the two stages refilled meanwhile; otherwise one barrier per block.
 //  * Key order inside a 32-key block is permuted (tau) so that the S^T output
 //    a lane holds is 16 consecutive keys of one query row: exactly the P^T
 //    operand of the P.V product. Plain-layout V reaches the V^T operand through
@@ -166,6 +166,9 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   auto vswz = [](int r) __attribute__((always_inline)) {
     return SPAN * ((r / KPR) % (NCK / SPAN));
   };
+  // K rows (key r of a 32-key block) are permuted the same way with a finer
+  // XOR: the S^T operand reads 16 bytes of each of 32 keys per half-wave.
+  auto kswz = [](int r) __attribute__((always_inline)) { return (r / KPR) % NCK; };
   // Direct-to-LDS loads per block: K, V and (quantized) one of scales. With
   // two row halves the first half's wave of a stream issues K and the
   // scales, the second half's wave V.
@@ -280,9 +283,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   };
 
   // Per-lane byte offsets of the direct-to-LDS loads (fixed for the kernel).
-  //  K, group gp, load n: lane l fetches 16 bytes of key (l % 16) ^ (8 gp) of
-  //    the group at row byte (4 n + l / 16) * 16; the XOR spreads the
-  //    consumer's 16-byte LDS reads over all banks.
+  //  K, group gp, load n: whole key rows, like plain V: row n * (1024 / RB) +
+  //    l / (RB / 16) of the group, LDS chunk l % (RB / 16) receiving global
+  //    chunk (l % (RB / 16)) ^ kswz(row in the block), so that the consumer's
+  //    16-byte reads of 32 different keys hit each bank at most twice.
   //  plain V, load n: row n * (1024 / RB) + l / (RB / 16), 16-byte column
   //    l % (RB / 16) (the group's rows, in key order).
   //  transposed V, load n: unit u = 2 n + l / 32 (d-block u / EB, 16-byte key
@@ -292,7 +296,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
     for (int n = 0; n < KIG; ++n)
-      koffs[gp][n] = (uint32_t)(((lane & 15) ^ (8 * gp)) * RB + (4 * n + (lane >> 4)) * 16);
+    {
+      const int row = n * (1024 / RB) + lane / (RB / 16);
+      koffs[gp][n] = (uint32_t)(row * RB + (((lane % (RB / 16)) ^ kswz(16 * gp + row)) * 16));
+    }
   uint32_t voffs[NVL];
   {
     const int dstride = (p.paged ? (1 << p.bs_shift) : p.kv_cap) * EB;
@@ -364,10 +371,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     }
   };
 
-  // Consumer side of the K layout: key tau(i32) sits in group tau / 16 at
-  // position (tau % 16) ^ (8 group); its 16-byte chunk j of the row is at
-  // + j * 256.
-  const int kread = ((tau(i32) >> 4) * KIG) * 1024 + ((tau(i32) & 15) ^ (8 * (tau(i32) >> 4))) * 16;
+  // Consumer side of the K layout: row tau(i32) of the block; its 16-byte
+  // chunk j sits at j ^ kswz(tau). This lane reads chunks hh * NCH + c.
+  const int krow = tau(i32) * RB;
+  const int kx = (hh * NCH) ^ kswz(tau(i32));
   // B operand of S^T = K Q^T, read from LDS at every block: k-step kk of lane
   // (i32, hh) is row 32 rh + i32, d in [hh D/2 + 8 kk, +8).
   const int qoff0 = (32 * rh + i32) * QS + hh * (D / 2);
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     asm volatile("" : "+v"(qoff));                // re-read Q from LDS every block
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const u32x4 kc = *reinterpret_cast<const u32x4*>(S + kread + (hh * NCH + c) * 256);
+      const u32x4 kc = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
       constexpr int KPC = 16 / (8 * EB);          // k-steps per 16-byte chunk
 #pragma unroll
       for (int h2 = 0; h2 < KPC; ++h2) {
@@ -573,39 +580,69 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 
   // ---- the key loop ----------------------------------------------------------
   // Key stream sid takes the split's 32-key blocks sid, sid + 4, ...; both
-  // row halves of a stream consume every block of it. All waves step
-  // together, one workgroup barrier per step (the same number of steps for
-  // every wave): at step j the barrier publishes block j (each wave waited
-  // for its own loads of it) and frees the stage of block j - 1, into which
-  // block j + NS - 1 is then loaded.
+  // row halves of a stream consume every block of it. All waves step together
+  // through workgroup barriers (the same number for every wave); each wave
+  // first waits for its own loads of the blocks a barrier publishes.
   const int nblk = hi > lo ? (hi - lo + 31) / 32 : 0;
   const int mine = nblk > sid ? (nblk - 1 - sid) / 4 + 1 : 0;
   const int steps = (nblk + 3) / 4;
   auto t0_of = [&](int j) __attribute__((always_inline)) { return lo + (sid + 4 * j) * 32; };
+  if constexpr (NS >= 4) {
+    // Two blocks per barrier: it publishes blocks j, j + 1 and frees the
+    // stages of j - 2, j - 1, into which j + 2 and j + 3 are loaded while j
+    // and j + 1 are computed (their loads go out between the two matrix-core
+    // phases of each block, so the waves do not all queue on the vector
+    // memory unit at once). Page ids are read one barrier step ahead.
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
-  // page ids of the block issued at the next step, read one step ahead
-  Ids ids{0, 0};
-  if (NS - 1 < mine) ids = load_ids(t0_of(NS - 1));
-  for (int j = 0; j < steps; ++j) {
-    {
-      const int r = mine - 1 - j;                 // own blocks issued after block j: min(r, NS - 2)
-      wait_own(r < NS - 2 ? r : NS - 2);
+    for (int j = 0; j < 2; ++j)
+      if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
+    Ids ids0{0, 0}, ids1{0, 0};
+    if (2 < mine) ids0 = load_ids(t0_of(2));
+    if (3 < mine) ids1 = load_ids(t0_of(3));
+    for (int j = 0; j < steps; j += 2) {
+      wait_vm<0>();                               // blocks j, j + 1: everything this wave issued
+      __syncthreads();
+      auto loads0 = [&]() __attribute__((always_inline)) {
+        if (j + 2 < mine) issue(t0_of(j + 2), ids0, (j + 2) % NS);
+      };
+      auto loads1 = [&]() __attribute__((always_inline)) {
+        if (j + 3 < mine) issue(t0_of(j + 3), ids1, (j + 3) % NS);
+      };
+      if (j < mine)
+        compute(t0_of(j), j % NS, loads0);
+      else
+        loads0();
+      if (j + 1 < mine)
+        compute(t0_of(j + 1), (j + 1) % NS, loads1);
+      else
+        loads1();
+      if (j + 4 < mine) ids0 = load_ids(t0_of(j + 4));
+      if (j + 5 < mine) ids1 = load_ids(t0_of(j + 5));
     }
-    __syncthreads();
-    const int jn = j + NS - 1;
-    // the loads of block jn go out between the two matrix-core phases of
-    // block j, so that the eight waves do not all queue on the vector memory
-    // unit right after the barrier
-    auto next_loads = [&]() __attribute__((always_inline)) {
-      if (jn < mine) issue(t0_of(jn), ids, jn % NS);
-    };
-    if (j < mine)
-      compute(t0_of(j), j % NS, next_loads);
-    else
-      next_loads();
-    if (jn + 1 < mine) ids = load_ids(t0_of(jn + 1));
+  } else {
+    // One block per barrier: it publishes block j and frees the stage of
+    // block j - 1, into which block j + NS - 1 is loaded while j is computed.
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
+    Ids ids{0, 0};                                 // page ids of the next step's block
+    if (NS - 1 < mine) ids = load_ids(t0_of(NS - 1));
+    for (int j = 0; j < steps; ++j) {
+      {
+        const int r = mine - 1 - j;               // own blocks issued after block j: min(r, NS - 2)
+        wait_own(r < NS - 2 ? r : NS - 2);
+      }
+      __syncthreads();
+      const int jn = j + NS - 1;
+      auto next_loads = [&]() __attribute__((always_inline)) {
+        if (jn < mine) issue(t0_of(jn), ids, jn % NS);
+      };
+      if (j < mine)
+        compute(t0_of(j), j % NS, next_loads);
+      else
+        next_loads();
+      if (jn + 1 < mine) ids = load_ids(t0_of(jn + 1));
+    }
   }
 
   // ---- merge the four streams' states through LDS (stream order) ------------
