@@ -30,10 +30,15 @@
 //    operand of the P.V product. Plain-layout V reaches the V^T operand through
 //    gfx950's transposing LDS reads (8 keys of one d per lane), from rows whose
 //    16-byte chunks the loads permute to keep those reads conflict-free.
-//  * FP8 codes become BF16 with v_cvt_scalef32_pk_bf16_fp8 and INT8 codes via
-//    fp32, both exactly; the per-token K scale multiplies the logits and the
-//    per-token V scale the probabilities, so the only rounding besides fp32
-//    accumulation is P -> bf16.
+//  * FP8 K feeds the fp8 matrix cores directly (v_mfma_scale_f32_32x32x64_
+//    f8f6f4): Q is split once per workgroup, per row and 32-d block, into an
+//    fp8 high part and an fp8 residual with power-of-two block scales, which
+//    reproduces every bf16 element within 2^13 of its block maximum exactly;
+//    these products accumulate at about 2^-14 of the sum of their magnitudes
+//    (measured), not at fp32. INT8 and BF16 K convert to bf16 (exactly) for
+//    v_mfma_f32_32x32x16_bf16. V codes always convert to bf16 exactly. The
+//    per-token K scale multiplies the logits and the per-token V scale the
+//    probabilities, so the other rounding is P -> bf16.
 //  * The softmax is online with lazy rescaling: the running maximum of a row
 //    is only raised (and acc, l rescaled) when a logit exceeds it by more than
 //    2^8, which a wave vote detects; the row max needs one cross-half shuffle.
@@ -52,6 +57,8 @@ namespace skv {
 namespace {
 
 typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // MFMA row i of the K operand of a 32-key block holds key tau(i); then output
@@ -146,7 +153,12 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int U = DB * EB;                     // transposed V: 512-byte units per group
   static_assert(RB >= 64 && RB % 64 == 0, "key rows of 64, 128 or 256 bytes");
   constexpr int QS = D + 8;                      // LDS row stride of Q (bf16), padded
-  constexpr int QBYTES = ROWS * QS * 2;
+  // FP8 K: S^T = K Q^T runs on the fp8 matrix cores (32x32x64 with block
+  // scales), Q split once per workgroup into an fp8 high part and an fp8
+  // residual; other codes convert K to bf16.
+  constexpr bool F8QK = __is_same(KT, FP8);
+  constexpr int QS8 = D + 16;                    // LDS row stride of the fp8 Q parts, padded
+  constexpr int QBYTES = F8QK ? 2 * ROWS * QS8 + ROWS * (D / 32) * 2 : ROWS * QS * 2;
   constexpr int BUDGET = 156 * 1024;
   constexpr int NS0 = (BUDGET - QBYTES) / (4 * STAGE);
   constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per key stream
@@ -208,16 +220,79 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // Query rows of the group -> LDS (bf16, rows padded by 16 bytes); rows past
   // rho are zero. The B operand of S^T = K Q^T is read back per k-step:
   // lane holds row i32 of the wave's rows, d in [hh * D/2 + 8 kk, +8).
-  for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
-    const int row = idx / (D / 8), c8 = idx - row * (D / 8);
-    const int r = rbase + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (r < p.rho) {
-      int j, hq;
-      row_jh(p, g, r, &j, &hq);
-      x = ld16(reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 8 * c8));
+  uint8_t* qh_s = reinterpret_cast<uint8_t*>(smem + SMEM0);   // fp8 Q parts (F8QK)
+  uint8_t* ql_s = qh_s + ROWS * QS8;
+  uint8_t* qe_s = ql_s + ROWS * QS8;             // [row][32-d block]: E8M0 scales of both parts
+  if constexpr (F8QK) {
+    // Per (row, 32-d block): x = q 2^-e with max |x| in [128, 256), x = hi +
+    // lo / 16 with hi = fp8(x) and lo = fp8(16 (x - hi)). A bf16 q has 8
+    // significant bits, hi keeps 4 and the remainder fits the 4 of lo, so the
+    // split is exact for every element within 2^13 of the block's maximum;
+    // the products then carry the scales 2^e and 2^(e - 4).
+    for (int idx = tid; idx < ROWS * (D / 32); idx += NT) {
+      const int row = idx / (D / 32), blk = idx - row * (D / 32);
+      const int r = rbase + row;
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+      if (r < p.rho) {
+        int j, hq;
+        row_jh(p, g, r, &j, &hq);
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x4 w = ld16(src + 8 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
+            x[8 * u + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      int e = 0;
+      if (amax > 0.0f) e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 7;
+      e = e < -123 ? -123 : (e > 127 ? 127 : e);
+      const float sc = __builtin_ldexpf(1.0f, -e);
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a0 = x[4 * k] * sc, a1 = x[4 * k + 1] * sc, a2 = x[4 * k + 2] * sc, a3 = x[4 * k + 3] * sc;
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, h, true);
+        const float r0 = 16.0f * (a0 - __builtin_amdgcn_cvt_f32_fp8(h, 0));
+        const float r1 = 16.0f * (a1 - __builtin_amdgcn_cvt_f32_fp8(h, 1));
+        const float r2 = 16.0f * (a2 - __builtin_amdgcn_cvt_f32_fp8(h, 2));
+        const float r3 = 16.0f * (a3 - __builtin_amdgcn_cvt_f32_fp8(h, 3));
+        int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+        l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+        hw[k] = (uint32_t)h;
+        lw[k] = (uint32_t)l;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        *reinterpret_cast<u32x4*>(&qh_s[row * QS8 + 32 * blk + 16 * u]) =
+            u32x4{hw[4 * u], hw[4 * u + 1], hw[4 * u + 2], hw[4 * u + 3]};
+        *reinterpret_cast<u32x4*>(&ql_s[row * QS8 + 32 * blk + 16 * u]) =
+            u32x4{lw[4 * u], lw[4 * u + 1], lw[4 * u + 2], lw[4 * u + 3]};
+      }
+      qe_s[(row * (D / 32) + blk) * 2] = (uint8_t)(e + 127);
+      qe_s[(row * (D / 32) + blk) * 2 + 1] = (uint8_t)(e - 4 + 127);
     }
-    *reinterpret_cast<u32x4*>(&q_s[row * QS + 8 * c8]) = x;
+  } else {
+    for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
+      const int row = idx / (D / 8), c8 = idx - row * (D / 8);
+      const int r = rbase + row;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < p.rho) {
+        int j, hq;
+        row_jh(p, g, r, &j, &hq);
+        x = ld16(reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 8 * c8));
+      }
+      *reinterpret_cast<u32x4*>(&q_s[row * QS + 8 * c8]) = x;
+    }
   }
   // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
   const int wrow0 = rbase + 32 * rh;
@@ -378,6 +453,20 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // B operand of S^T = K Q^T, read from LDS at every block: k-step kk of lane
   // (i32, hh) is row 32 rh + i32, d in [hh D/2 + 8 kk, +8).
   const int qoff0 = (32 * rh + i32) * QS + hh * (D / 2);
+  // fp8 path: k-step ks (64 d) of lane (i32, hh) covers d in [64 ks + 32 hh,
+  // +32) of K (row tau(i32)) and of Q (row 32 rh + i32): one 32-d block, whose
+  // two E8M0 scales are loop-invariant per lane.
+  constexpr int KS8 = D / 64;
+  int qsh[KS8], qsl[KS8];
+  const int q8off = (32 * rh + i32) * QS8 + 16 * hh;
+  if constexpr (F8QK) {                          // (the split Q rows are in LDS: barrier above)
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      const int blk = 2 * ks + hh;
+      qsh[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2];
+      qsl[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2 + 1];
+    }
+  }
 
   // ---- one 32-key block in stage st ------------------------------------------
   // Blocks wholly inside the split and inside every row's visible range skip
@@ -391,24 +480,58 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     const int kb = 16 * hh;                       // first key of this lane's 16
     // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
     floatx16 s;
+    if constexpr (F8QK) {
+      int qo = q8off;
+      asm volatile("" : "+v"(qo));                // re-read Q from LDS every block
+      u32x4 ka[KS8][2], qa[KS8][2], qb[KS8][2];
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = 4 * ks + hh + 2 * u;       // 16-byte chunk of the key row
+          ka[ks][u] = *reinterpret_cast<const u32x4*>(S + krow + ((c ^ kswz(tau(i32))) * 16));
+          qa[ks][u] = *reinterpret_cast<const u32x4*>(&qh_s[qo + 64 * ks + 32 * u]);
+          qb[ks][u] = *reinterpret_cast<const u32x4*>(&ql_s[qo + 64 * ks + 32 * u]);
+        }
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks) {
+        const i32x8 a = __builtin_bit_cast(i32x8, u32x8{ka[ks][0][0], ka[ks][0][1], ka[ks][0][2], ka[ks][0][3],
+                                                            ka[ks][1][0], ka[ks][1][1], ka[ks][1][2], ka[ks][1][3]});
+        const i32x8 bh = __builtin_bit_cast(i32x8, u32x8{qa[ks][0][0], qa[ks][0][1], qa[ks][0][2], qa[ks][0][3],
+                                                             qa[ks][1][0], qa[ks][1][1], qa[ks][1][2], qa[ks][1][3]});
+        const i32x8 bl = __builtin_bit_cast(i32x8, u32x8{qb[ks][0][0], qb[ks][0][1], qb[ks][0][2], qb[ks][0][3],
+                                                             qb[ks][1][0], qb[ks][1][1], qb[ks][1][2], qb[ks][1][3]});
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bh, ks == 0 ? floatx16{} : s, 0, 0, 0, 127, 0, qsh[ks]);
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bl, s, 0, 0, 0, 127, 0, qsl[ks]);
+      }
+    } else {
     int qoff = qoff0;
     asm volatile("" : "+v"(qoff));                // re-read Q from LDS every block
+    // all operand reads first, so that their latency overlaps instead of
+    // stalling each product
+    constexpr int KPC = 16 / (8 * EB);            // k-steps per 16-byte chunk
+    constexpr int KS = NCH * KPC;                 // k-steps of 16 d
+    u32x4 kc[NCH];
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kc[c] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff + 8 * kk]));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const u32x4 kc = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
-      constexpr int KPC = 16 / (8 * EB);          // k-steps per 16-byte chunk
 #pragma unroll
       for (int h2 = 0; h2 < KPC; ++h2) {
         const int kk = c * KPC + h2;
         bf16x8 kf;
         if constexpr (EB == 1) {
-          kf = cvt8<KT>(kc[2 * h2], kc[2 * h2 + 1], 0u, 0u);
+          kf = cvt8<KT>(kc[c][2 * h2], kc[c][2 * h2 + 1], 0u, 0u);
         } else {
-          kf = cvt8<KT>(kc[0], kc[1], kc[2], kc[3]);
+          kf = cvt8<KT>(kc[c][0], kc[c][1], kc[c][2], kc[c][3]);
         }
-        const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff + 8 * kk]));
-        s = mfma(kf, qf, kk == 0 ? floatx16{} : s);
+        s = mfma(kf, qf[kk], kk == 0 ? floatx16{} : s);
       }
+    }
     }
     mid();                                        // e.g. the next block's loads
     // ---- per-key scales (K scale folded into c, V scale into the probabilities)
