@@ -25,6 +25,11 @@
 //    a stream one issues the K and scale loads, the other the V loads. With
 //    four stages one workgroup barrier per two blocks publishes them and
 //    frees the two stages refilled meanwhile; otherwise one barrier per block.
+//  * Per block a wave reads from LDS only its K operand rows, V (issued
+//    before the softmax, whose vector work hides the read latency) and one K
+//    and one V scale per lane; DPP row broadcasts hand each lane the scales
+//    of its 16 keys. Q (fp8 parts or bf16) stays in registers for the whole
+//    key loop, and the accumulators stay in arch VGPRs.
 //  * Key order inside a 32-key block is permuted (tau) so that the S^T output
 //    a lane holds is 16 consecutive keys of one query row: exactly the P^T
 //    operand of the P.V product. Plain-layout V reaches the V^T operand through
@@ -49,6 +54,7 @@
 //    split.
 
 #include <type_traits>
+#include <utility>
 
 #include "skv_device.h"
 
@@ -64,6 +70,37 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // MFMA row i of the K operand of a 32-key block holds key tau(i); then output
 // value v of a lane in wave half h is key 16 h + v.
 __device__ __forceinline__ int tau(int i) { return ((i & 4) << 2) | ((i >> 1) & 0xC) | (i & 3); }
+
+// y[v] = x of lane 16 (lane / 16) + v: a broadcast inside each 16-lane row
+// (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, true));
+}
+template <int... V>
+__device__ __forceinline__ void row_bcast16(float x, float (&y)[16], std::integer_sequence<int, V...>) {
+  ((y[V] = row_bcast<V>(x)), ...);
+}
+// y[B + v] = (x of lane 16 (lane / 16) + B + v) * a[B + v], v < 8: the
+// broadcast rides on the multiply (v_mul_f32_dpp). The leading s_nop covers
+// the wait states a DPP source needs after a VALU write.
+template <int B>
+__device__ __forceinline__ void row_bcast_mul8(float x, const float (&a)[16], float (&y)[16]) {
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %8, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %8, %10 row_newbcast:%18 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %2, %8, %11 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %8, %12 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %4, %8, %13 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %5, %8, %14 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %6, %8, %15 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %7, %8, %16 row_newbcast:%24 row_mask:0xf bank_mask:0xf"
+      : "=&v"(y[B]), "=&v"(y[B + 1]), "=&v"(y[B + 2]), "=&v"(y[B + 3]), "=&v"(y[B + 4]), "=&v"(y[B + 5]),
+        "=&v"(y[B + 6]), "=&v"(y[B + 7])
+      : "v"(x), "v"(a[B]), "v"(a[B + 1]), "v"(a[B + 2]), "v"(a[B + 3]), "v"(a[B + 4]), "v"(a[B + 5]),
+        "v"(a[B + 6]), "v"(a[B + 7]), "n"(B), "n"(B + 1), "n"(B + 2), "n"(B + 3), "n"(B + 4), "n"(B + 5),
+        "n"(B + 6), "n"(B + 7));
+}
 
 template <class KT>
 __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -459,12 +496,27 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int KS8 = D / 64;
   int qsh[KS8], qsl[KS8];
   const int q8off = (32 * rh + i32) * QS8 + 16 * hh;
+  // Q stays in registers for the whole key loop (fp8 parts, or bf16).
+  u32x4 qa[KS8][2], qb[KS8][2];
+  constexpr int KPC = 16 / (8 * EB);              // k-steps per 16-byte chunk
+  constexpr int KS = NCH * KPC;                   // k-steps of 16 d
+  bf16x8 qf[F8QK ? 1 : KS];
+  if constexpr (!F8QK) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
+  }
   if constexpr (F8QK) {                          // (the split Q rows are in LDS: barrier above)
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) {
       const int blk = 2 * ks + hh;
       qsh[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2];
       qsl[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2 + 1];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        qa[ks][u] = *reinterpret_cast<const u32x4*>(&qh_s[q8off + 64 * ks + 32 * u]);
+        qb[ks][u] = *reinterpret_cast<const u32x4*>(&ql_s[q8off + 64 * ks + 32 * u]);
+      }
     }
   }
 
@@ -481,17 +533,13 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
     floatx16 s;
     if constexpr (F8QK) {
-      int qo = q8off;
-      asm volatile("" : "+v"(qo));                // re-read Q from LDS every block
-      u32x4 ka[KS8][2], qa[KS8][2], qb[KS8][2];
+      u32x4 ka[KS8][2];
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int c = 4 * ks + hh + 2 * u;       // 16-byte chunk of the key row
           ka[ks][u] = *reinterpret_cast<const u32x4*>(S + krow + ((c ^ kswz(tau(i32))) * 16));
-          qa[ks][u] = *reinterpret_cast<const u32x4*>(&qh_s[qo + 64 * ks + 32 * u]);
-          qb[ks][u] = *reinterpret_cast<const u32x4*>(&ql_s[qo + 64 * ks + 32 * u]);
         }
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks) {
@@ -505,19 +553,11 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bl, s, 0, 0, 0, 127, 0, qsl[ks]);
       }
     } else {
-    int qoff = qoff0;
-    asm volatile("" : "+v"(qoff));                // re-read Q from LDS every block
     // all operand reads first, so that their latency overlaps instead of
     // stalling each product
-    constexpr int KPC = 16 / (8 * EB);            // k-steps per 16-byte chunk
-    constexpr int KS = NCH * KPC;                 // k-steps of 16 d
     u32x4 kc[NCH];
-    bf16x8 qf[KS];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kc[c] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff + 8 * kk]));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
@@ -534,35 +574,77 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     }
     }
     mid();                                        // e.g. the next block's loads
-    // ---- per-key scales (K scale folded into c, V scale into the probabilities)
-    float c[16], sv[16];
-    if constexpr (QUANT) {
-      const float* sc = reinterpret_cast<const float*>(S + KSZ + VSZ);
+    // ---- V^T operand reads, ahead of the softmax that hides their latency:
+    // xr[db] holds d-block db (transposed V: EB 16-byte key runs; plain V: per
+    // key half kh, words 4 kh + [0, 4))
+    uint32_t xr[DB][8];
+    if constexpr (VT) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(sc + kb + 4 * q);
-        const floatx4 z = *reinterpret_cast<const floatx4*>(sc + 32 + kb + 4 * q);
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[4 * q + e] = a[e] * p.scale_log2;
-          sv[4 * q + e] = z[e];
+        for (int e = 0; e < EB; ++e) {
+          const u32x4 vc = *reinterpret_cast<const u32x4*>(S + KSZ + hh * U * 512 + (db * EB + e) * 512 + i32 * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xr[db][4 * e + q] = vc[q];
+        }
+    } else {
+      // transposing LDS reads: in each 16-lane group (wave half hh, d half mh
+      // of a 32-d block), lane i gets 8 (8-bit) or 4 (bf16) consecutive keys
+      // of d = 32 db + 16 mh + i; lane r of the group supplies the address of
+      // the row segment that the transpose distributes (key 2 j + r / 2 ...)
+      const int gi = lane & 15;
+      const int mh = (lane >> 4) & 1;
+      const char* vg = S + KSZ + hh * VGS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          if constexpr (EB == 1) {
+            const int key = 8 * kh + (gi >> 1);
+            const int c = 2 * db + mh;
+            const char* a8 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
+            const v2i32 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i32*)(a8));
+            xr[db][4 * kh] = (uint32_t)t[0];
+            xr[db][4 * kh + 1] = (uint32_t)t[1];
+            xr[db][4 * kh + 2] = xr[db][4 * kh + 3] = 0u;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int key = 8 * kh + 4 * q + (gi >> 2);
+              const int c = 4 * db + 2 * mh + ((gi & 3) >> 1);
+              const char* a16 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
+              const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4i16*)(a16));
+              const u32x2 u = __builtin_bit_cast(u32x2, t);
+              xr[db][4 * kh + 2 * q] = u[0];
+              xr[db][4 * kh + 2 * q + 1] = u[1];
+            }
+          }
         }
       }
+    }
+    // ---- per-key scales (K scale folded into c, V scale into the probabilities):
+    // lane l reads the scales of key kb + l % 16 only; row broadcasts hand
+    // each lane those of its 16 keys
+    float c[16];
+    float xv = 1.0f;
+    const int nv = hi - (t0 + kb);                // keys of this lane's 16 inside the split
+    if constexpr (QUANT) {
+      const float* sc = reinterpret_cast<const float*>(S + KSZ + VSZ);
+      const float xk = sc[kb + (lane & 15)] * p.scale_log2;
+      xv = sc[32 + kb + (lane & 15)];
+      if (boundary) {
+        // the V scales of keys past the split may be NaN: zero them, so masked
+        // keys give exactly zero (the empty asm keeps this a branch)
+        int n = nv;
+        asm volatile("" : "+v"(n));
+        xv = ((lane & 15) < n) ? xv : 0.0f;
+      }
+      row_bcast16(xk, c, std::make_integer_sequence<int, 16>{});
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        c[v] = p.scale_log2;
-        sv[v] = 1.0f;
-      }
-    }
-    const int nv = hi - (t0 + kb);                // keys of this lane's 16 inside the split
-    if (boundary) {
-      // the V scales of keys past the split may be NaN: zero them, so masked
-      // keys give exactly zero (the empty asm keeps this a branch)
-      int n = nv;
-      asm volatile("" : "+v"(n));
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sv[v] = (v < n) ? sv[v] : 0.0f;
+      for (int v = 0; v < 16; ++v) c[v] = p.scale_log2;
     }
     // ---- logits t = s * c - mu (mu: the running reference maximum), so that
     // the probability is exp2(t); boundary blocks then replace masked logits
@@ -587,7 +669,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     const bool need = (mrun == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
     if (__any(need)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
       const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
       const float mnew = fmaxf(mrun, mt + mu);
       const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
@@ -601,20 +683,26 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       for (int v = 0; v < 16; ++v) s[v] -= shift;
       mrun = mnew;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
     }
     // ---- probabilities times the V scale as the bf16 P^T operand
     bf16x8 pf[2];
     {
       float lsum = 0.0f;
-      float pv[16];
+      float pe[16], pv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pe = fexp2(s[v]);
-        lsum += pe;
-        pv[v] = QUANT ? pe * sv[v] : pe;
+        pe[v] = fexp2(s[v]);
+        lsum += pe[v];
       }
       lrun += lsum;
+      if constexpr (QUANT) {
+        row_bcast_mul8<0>(xv, pe, pv);
+        row_bcast_mul8<8>(xv, pe, pv);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pv[v] = pe[v];
+      }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const u32x4 pk = {pack_bf16x2(pv[8 * kh], pv[8 * kh + 1]), pack_bf16x2(pv[8 * kh + 2], pv[8 * kh + 3]),
@@ -624,81 +712,39 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     }
     // ---- O^T += V^T P^T (V codes of keys past the split zeroed on boundary
     // blocks: they may be NaN-poisoned)
-    if constexpr (VT) {
+    if (boundary) {
+      asm volatile("");
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        uint32_t x[4 * EB];
+        if constexpr (VT) {
 #pragma unroll
-        for (int e = 0; e < EB; ++e) {
-          const u32x4 vc = *reinterpret_cast<const u32x4*>(S + KSZ + hh * U * 512 + (db * EB + e) * 512 + i32 * 16);
+          for (int q = 0; q < 4 * EB; ++q) xr[db][q] = keep_bytes(xr[db][q], q * (4 / EB), nv, 4 / EB);
+        } else {
+          constexpr int PW = 4 / EB;               // keys per word
 #pragma unroll
-          for (int q = 0; q < 4; ++q) x[4 * e + q] = vc[q];
-        }
-        if (boundary) {
-          asm volatile("");
+          for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int q = 0; q < 4 * EB; ++q) x[q] = keep_bytes(x[q], q * (4 / EB), nv, 4 / EB);
-        }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          bf16x8 vf;
-          if constexpr (EB == 1) {
-            vf = cvt8<KT>(x[2 * kh], x[2 * kh + 1], 0u, 0u);
-          } else {
-            vf = cvt8<KT>(x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]);
-          }
-          acc[db] = mfma(vf, pf[kh], acc[db]);
-        }
-      }
-    } else {
-      // transposing LDS reads: in each 16-lane group (wave half hh, d half mh
-      // of a 32-d block), lane i gets 8 (8-bit) or 4 (bf16) consecutive keys
-      // of d = 32 db + 16 mh + i; lane r of the group supplies the address of
-      // the row segment that the transpose distributes (key 2 j + r / 2 ...)
-      const int gi = lane & 15;
-      const int mh = (lane >> 4) & 1;
-      const char* vg = S + KSZ + hh * VGS;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          uint32_t x[4];
-          if constexpr (EB == 1) {
-            const int key = 8 * kh + (gi >> 1);
-            const int c = 2 * db + mh;
-            const char* a8 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
-            const v2i32 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) v2i32*)(a8));
-            x[0] = (uint32_t)t[0];
-            x[1] = (uint32_t)t[1];
-            x[2] = x[3] = 0u;
-          } else {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int key = 8 * kh + 4 * q + (gi >> 2);
-              const int c = 4 * db + 2 * mh + ((gi & 3) >> 1);
-              const char* a16 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
-              const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) v4i16*)(a16));
-              const u32x2 u = __builtin_bit_cast(u32x2, t);
-              x[2 * q] = u[0];
-              x[2 * q + 1] = u[1];
-            }
-          }
-          if (boundary) {
-            asm volatile("");
-            constexpr int PW = 4 / EB;                 // keys per word
-#pragma unroll
-            for (int q = 0; q < 2 * EB; ++q) x[q] = keep_bytes(x[q], 8 * kh + q * PW, nv, PW);
-          }
-          acc[db] = mfma(cvt8<KT>(x[0], x[1], x[2], x[3]), pf[kh], acc[db]);
+            for (int q = 0; q < 2 * EB; ++q) xr[db][4 * kh + q] = keep_bytes(xr[db][4 * kh + q], 8 * kh + q * PW, nv, PW);
         }
       }
     }
-    // The accumulators only meet VALU code in the rare rescale and at the
-    // end: keep them in AGPRs across blocks.
 #pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(acc[db]));
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 vf;
+        if constexpr (VT && EB == 1) {
+          vf = cvt8<KT>(xr[db][2 * kh], xr[db][2 * kh + 1], 0u, 0u);
+        } else {
+          vf = cvt8<KT>(xr[db][4 * kh], xr[db][4 * kh + 1], xr[db][4 * kh + 2], xr[db][4 * kh + 3]);
+        }
+        acc[db] = mfma(vf, pf[kh], acc[db]);
+      }
+    // The accumulators only meet VALU code in the rare rescale and at the
+    // end: keep them in one register assignment across blocks (arch VGPRs:
+    // with no AGPR use the whole register budget goes to them).
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
   };
 
   // ---- the key loop ----------------------------------------------------------
