@@ -119,6 +119,7 @@ extern "C" {
 #define SKV_ERR_UNSUPPORTED (-6)   /* valid request this build does not implement */
 #define SKV_ERR_LAUNCH (-7)        /* the HIP runtime rejected a kernel launch */
 #define SKV_ERR_PLAN (-8)          /* inconsistent plan hints or metadata sizes */
+#define SKV_ERR_ALIGN (-9)         /* partials.acc is not 16-byte aligned */
 
 typedef enum skv_dtype {
   SKV_F32 = 0,
@@ -168,7 +169,9 @@ typedef struct skv_args {
 } skv_args;
 
 /* Caller-owned partial-record buffers (device memory), sized by
- * skv_workspace_size for `capacity_slots` records. */
+ * skv_workspace_size for `capacity_slots` records. `acc` must be 16-byte
+ * aligned (its records are written and read as 4-float vectors);
+ * SKV_ERR_ALIGN otherwise. */
 typedef struct skv_partials {
   float* m;
   float* l;

@@ -69,6 +69,7 @@ int check_args(const skv_desc* d, const skv_args* a, int paged) {
 int check_partials(const skv_desc* d, const skv_partials* p, int64_t slots) {
   if (!p) return SKV_ERR_NULL;
   if (!p->m || !p->l || !p->acc) return SKV_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(p->acc) % 16 != 0) return SKV_ERR_ALIGN;
   if (p->capacity_slots < slots) return SKV_ERR_CAPACITY;
   return SKV_OK;
 }
@@ -240,6 +241,7 @@ const char* skv_status_str(int status) {
     case SKV_ERR_UNSUPPORTED: return "unsupported combination for the requested kernel family";
     case SKV_ERR_LAUNCH: return "kernel launch failed";
     case SKV_ERR_PLAN: return "inconsistent plan hints or metadata";
+    case SKV_ERR_ALIGN: return "partials.acc is not 16-byte aligned";
     default: return "unknown status";
   }
 }

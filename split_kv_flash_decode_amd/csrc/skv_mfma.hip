@@ -200,8 +200,8 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int NS0 = (BUDGET - QBYTES) / (4 * STAGE);
   constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per key stream
   constexpr int RING = 4 * NS * STAGE;
-  constexpr int PD = D + 1;                      // merge buffer row stride (floats)
-  constexpr int MERGE = ROWS * PD * 4;
+  constexpr int PD = D + 4;                      // merge buffer row stride (floats, 16-byte aligned)
+  constexpr int MERGE = 4 * ROWS * PD * 4;       // one slice per key stream
   constexpr int SMEM0 = RING > MERGE ? RING : MERGE;
   // Plain V rows sit in LDS with their 16-byte chunks permuted, chunk c of
   // row r (key r of a 16-key group) at c ^ vswz(r), so that the transposing
@@ -254,83 +254,9 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   const int rbase = rg * ROWS;
   const int nrow = (p.rho - rbase) < ROWS ? (p.rho - rbase) : ROWS;
 
-  // Query rows of the group -> LDS (bf16, rows padded by 16 bytes); rows past
-  // rho are zero. The B operand of S^T = K Q^T is read back per k-step:
-  // lane holds row i32 of the wave's rows, d in [hh * D/2 + 8 kk, +8).
   uint8_t* qh_s = reinterpret_cast<uint8_t*>(smem + SMEM0);   // fp8 Q parts (F8QK)
   uint8_t* ql_s = qh_s + ROWS * QS8;
   uint8_t* qe_s = ql_s + ROWS * QS8;             // [row][32-d block]: E8M0 scales of both parts
-  if constexpr (F8QK) {
-    // Per (row, 32-d block): x = q 2^-e with max |x| in [128, 256), x = hi +
-    // lo / 16 with hi = fp8(x) and lo = fp8(16 (x - hi)). A bf16 q has 8
-    // significant bits, hi keeps 4 and the remainder fits the 4 of lo, so the
-    // split is exact for every element within 2^13 of the block's maximum;
-    // the products then carry the scales 2^e and 2^(e - 4).
-    for (int idx = tid; idx < ROWS * (D / 32); idx += NT) {
-      const int row = idx / (D / 32), blk = idx - row * (D / 32);
-      const int r = rbase + row;
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
-      if (r < p.rho) {
-        int j, hq;
-        row_jh(p, g, r, &j, &hq);
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x4 w = ld16(src + 8 * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
-            x[8 * u + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-          }
-        }
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-      int e = 0;
-      if (amax > 0.0f) e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 7;
-      e = e < -123 ? -123 : (e > 127 ? 127 : e);
-      const float sc = __builtin_ldexpf(1.0f, -e);
-      uint32_t hw[8], lw[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float a0 = x[4 * k] * sc, a1 = x[4 * k + 1] * sc, a2 = x[4 * k + 2] * sc, a3 = x[4 * k + 3] * sc;
-        int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-        h = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, h, true);
-        const float r0 = 16.0f * (a0 - __builtin_amdgcn_cvt_f32_fp8(h, 0));
-        const float r1 = 16.0f * (a1 - __builtin_amdgcn_cvt_f32_fp8(h, 1));
-        const float r2 = 16.0f * (a2 - __builtin_amdgcn_cvt_f32_fp8(h, 2));
-        const float r3 = 16.0f * (a3 - __builtin_amdgcn_cvt_f32_fp8(h, 3));
-        int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-        l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
-        hw[k] = (uint32_t)h;
-        lw[k] = (uint32_t)l;
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        *reinterpret_cast<u32x4*>(&qh_s[row * QS8 + 32 * blk + 16 * u]) =
-            u32x4{hw[4 * u], hw[4 * u + 1], hw[4 * u + 2], hw[4 * u + 3]};
-        *reinterpret_cast<u32x4*>(&ql_s[row * QS8 + 32 * blk + 16 * u]) =
-            u32x4{lw[4 * u], lw[4 * u + 1], lw[4 * u + 2], lw[4 * u + 3]};
-      }
-      qe_s[(row * (D / 32) + blk) * 2] = (uint8_t)(e + 127);
-      qe_s[(row * (D / 32) + blk) * 2 + 1] = (uint8_t)(e - 4 + 127);
-    }
-  } else {
-    for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
-      const int row = idx / (D / 8), c8 = idx - row * (D / 8);
-      const int r = rbase + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < p.rho) {
-        int j, hq;
-        row_jh(p, g, r, &j, &hq);
-        x = ld16(reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 8 * c8));
-      }
-      *reinterpret_cast<u32x4*>(&q_s[row * QS + 8 * c8]) = x;
-    }
-  }
   // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
   const int wrow0 = rbase + 32 * rh;
   int vlo = 0, vhi = 0;
@@ -347,7 +273,6 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   }
   ilo = __builtin_amdgcn_readfirstlane(ilo);
   ihi = __builtin_amdgcn_readfirstlane(ihi);
-  __syncthreads();
 
   floatx16 acc[DB];
   float mrun = -INFINITY, lrun = 0.0f;
@@ -501,25 +426,105 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int KPC = 16 / (8 * EB);              // k-steps per 16-byte chunk
   constexpr int KS = NCH * KPC;                   // k-steps of 16 d
   bf16x8 qf[F8QK ? 1 : KS];
-  if constexpr (!F8QK) {
+  // Stage the group's query rows in LDS and read this lane's operand parts
+  // back (called once the first blocks' loads are in flight, so their
+  // latency overlaps the query loads).
+  auto stage_q = [&]() __attribute__((always_inline)) {
+    // Query rows of the group -> LDS (bf16, rows padded by 16 bytes); rows past
+    // rho are zero. The B operand of S^T = K Q^T is read back per k-step:
+    // lane holds row i32 of the wave's rows, d in [hh * D/2 + 8 kk, +8).
+    if constexpr (F8QK) {
+      // Per (row, 32-d block): x = q 2^-e with max |x| in [128, 256), x = hi +
+      // lo / 16 with hi = fp8(x) and lo = fp8(16 (x - hi)). A bf16 q has 8
+      // significant bits, hi keeps 4 and the remainder fits the 4 of lo, so the
+      // split is exact for every element within 2^13 of the block's maximum;
+      // the products then carry the scales 2^e and 2^(e - 4).
+      for (int idx = tid; idx < ROWS * (D / 32); idx += NT) {
+        const int row = idx / (D / 32), blk = idx - row * (D / 32);
+        const int r = rbase + row;
+        float x[32];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
-  }
-  if constexpr (F8QK) {                          // (the split Q rows are in LDS: barrier above)
+        for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+        if (r < p.rho) {
+          int j, hq;
+          row_jh(p, g, r, &j, &hq);
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
 #pragma unroll
-    for (int ks = 0; ks < KS8; ++ks) {
-      const int blk = 2 * ks + hh;
-      qsh[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2];
-      qsl[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2 + 1];
+          for (int u = 0; u < 4; ++u) {
+            const u32x4 w = ld16(src + 8 * u);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        qa[ks][u] = *reinterpret_cast<const u32x4*>(&qh_s[q8off + 64 * ks + 32 * u]);
-        qb[ks][u] = *reinterpret_cast<const u32x4*>(&ql_s[q8off + 64 * ks + 32 * u]);
+            for (int e = 0; e < 4; ++e) {
+              x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
+              x[8 * u + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+          }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        int e = 0;
+        if (amax > 0.0f) e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 7;
+        e = e < -123 ? -123 : (e > 127 ? 127 : e);
+        const float sc = __builtin_ldexpf(1.0f, -e);
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float a0 = x[4 * k] * sc, a1 = x[4 * k + 1] * sc, a2 = x[4 * k + 2] * sc, a3 = x[4 * k + 3] * sc;
+          int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+          h = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, h, true);
+          const float r0 = 16.0f * (a0 - __builtin_amdgcn_cvt_f32_fp8(h, 0));
+          const float r1 = 16.0f * (a1 - __builtin_amdgcn_cvt_f32_fp8(h, 1));
+          const float r2 = 16.0f * (a2 - __builtin_amdgcn_cvt_f32_fp8(h, 2));
+          const float r3 = 16.0f * (a3 - __builtin_amdgcn_cvt_f32_fp8(h, 3));
+          int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+          l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+          hw[k] = (uint32_t)h;
+          lw[k] = (uint32_t)l;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          *reinterpret_cast<u32x4*>(&qh_s[row * QS8 + 32 * blk + 16 * u]) =
+              u32x4{hw[4 * u], hw[4 * u + 1], hw[4 * u + 2], hw[4 * u + 3]};
+          *reinterpret_cast<u32x4*>(&ql_s[row * QS8 + 32 * blk + 16 * u]) =
+              u32x4{lw[4 * u], lw[4 * u + 1], lw[4 * u + 2], lw[4 * u + 3]};
+        }
+        qe_s[(row * (D / 32) + blk) * 2] = (uint8_t)(e + 127);
+        qe_s[(row * (D / 32) + blk) * 2 + 1] = (uint8_t)(e - 4 + 127);
+      }
+    } else {
+      for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
+        const int row = idx / (D / 8), c8 = idx - row * (D / 8);
+        const int r = rbase + row;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (r < p.rho) {
+          int j, hq;
+          row_jh(p, g, r, &j, &hq);
+          x = ld16(reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 8 * c8));
+        }
+        *reinterpret_cast<u32x4*>(&q_s[row * QS + 8 * c8]) = x;
       }
     }
-  }
+    __syncthreads();
+    if constexpr (!F8QK) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
+    }
+    if constexpr (F8QK) {                          // (the split Q rows are in LDS: barrier above)
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks) {
+        const int blk = 2 * ks + hh;
+        qsh[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2];
+        qsl[ks] = qe_s[((32 * rh + i32) * (D / 32) + blk) * 2 + 1];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          qa[ks][u] = *reinterpret_cast<const u32x4*>(&qh_s[q8off + 64 * ks + 32 * u]);
+          qb[ks][u] = *reinterpret_cast<const u32x4*>(&ql_s[q8off + 64 * ks + 32 * u]);
+        }
+      }
+    }
 
+  };
   // ---- one 32-key block in stage st ------------------------------------------
   // Blocks wholly inside the split and inside every row's visible range skip
   // all masking; on the others (a wave-uniform test) small branches mask
@@ -768,6 +773,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     Ids ids0{0, 0}, ids1{0, 0};
     if (2 < mine) ids0 = load_ids(t0_of(2));
     if (3 < mine) ids1 = load_ids(t0_of(3));
+    stage_q();
     for (int j = 0; j < steps; j += 2) {
       wait_vm<0>();                               // blocks j, j + 1: everything this wave issued
       __syncthreads();
@@ -796,6 +802,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
     Ids ids{0, 0};                                 // page ids of the next step's block
     if (NS - 1 < mine) ids = load_ids(t0_of(NS - 1));
+    stage_q();
     for (int j = 0; j < steps; ++j) {
       {
         const int r = mine - 1 - j;               // own blocks issued after block j: min(r, NS - 2)
@@ -840,40 +847,47 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       fin_s[row][1] = L;
     }
   }
+  // Each stream writes its weighted accumulators to its own slice; after one
+  // barrier every thread sums the four slices of its outputs in stream order.
 #pragma unroll
-  for (int ss = 0; ss < 4; ++ss) {
-    if (sid == ss) {
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int di = 8 * (v >> 2) + 4 * hh + (v & 3);
-          const int d = 32 * db + di;
-          const int idx = row * PD + d;
-          const float val = wgt * acc[db][v];
-          acc_s[idx] = (ss == 0) ? val : acc_s[idx] + val;
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * db + 8 * q + 4 * hh;       // values 4 q .. 4 q + 3: d .. d + 3
+      const floatx4 val = {wgt * acc[db][4 * q], wgt * acc[db][4 * q + 1], wgt * acc[db][4 * q + 2],
+                           wgt * acc[db][4 * q + 3]};
+      *reinterpret_cast<floatx4*>(&acc_s[(sid * ROWS + row) * PD + d]) = val;
     }
-    __syncthreads();
-  }
+  __syncthreads();
+  auto merged = [&](int rr, int d) __attribute__((always_inline)) {
+    floatx4 v = *reinterpret_cast<const floatx4*>(&acc_s[rr * PD + d]);
+#pragma unroll
+    for (int ss = 1; ss < 4; ++ss) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(&acc_s[(ss * ROWS + rr) * PD + d]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = v[e] + x[e];
+    }
+    return v;
+  };
 
   if (p.finalize) {
-    for (int idx = tid; idx < nrow * D; idx += NT) {
-      const int rr = idx / D, d = idx - (idx / D) * D;
+    for (int idx = tid; idx < nrow * (D / 4); idx += NT) {
+      const int rr = idx / (D / 4), d = 4 * (idx - rr * (D / 4));
       const int r = rbase + rr;
       int j, hq;
       row_jh(p, g, r, &j, &hq);
       const float s2 = p.has_sink ? p.sinks[hq] * kLog2e : 0.0f;
-      store_o1(p, qo_idx(p, b, j, hq, d),
-               finalize_one(fin_s[rr][0], fin_s[rr][1], acc_s[rr * PD + d], p.has_sink, s2));
+      const floatx4 v = merged(rr, d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        store_o1(p, qo_idx(p, b, j, hq, d + e), finalize_one(fin_s[rr][0], fin_s[rr][1], v[e], p.has_sink, s2));
     }
   } else {
     const int64_t slot = (int64_t)it.slot_item * p.Hkv + g;
-    for (int idx = tid; idx < nrow * D; idx += NT) {
-      const int rr = idx / D, d = idx - (idx / D) * D;
+    for (int idx = tid; idx < nrow * (D / 4); idx += NT) {
+      const int rr = idx / (D / 4), d = 4 * (idx - rr * (D / 4));
       const int64_t rec = slot * p.rho + rbase + rr;
-      p.pacc[rec * D + d] = acc_s[rr * PD + d];
+      *reinterpret_cast<floatx4*>(&p.pacc[rec * D + d]) = merged(rr, d);
       if (d == 0) {
         p.pm[rec] = fin_s[rr][0];
         p.pl[rec] = fin_s[rr][1];

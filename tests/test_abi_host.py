@@ -80,10 +80,21 @@ def test_partial_capacity_is_checked():
     d = _desc()
     need = skv.uniform_slots(d, 4)
     assert need == 2 * 4 * 1
-    p = skv.Partials(1, 1, 1, need - 1)
+    p = skv.Partials(16, 16, 16, need - 1)
     assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == -5
-    p = skv.Partials(1, 1, 1, need)
+    p = skv.Partials(16, 16, 16, need)
     assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == 0
+
+
+def test_partial_accumulators_must_be_16_byte_aligned():
+    d = _desc()
+    need = skv.uniform_slots(d, 4)
+    for off in (4, 8, 12):
+        p = skv.Partials(16, 16, 4096 + off, need)
+        assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == -9
+    p = skv.Partials(16, 16, 4096, need)
+    assert skv.lib().skv_validate(ctypes.byref(d), 1, 4, ctypes.byref(p)) == 0
+    assert "aligned" in skv.status_str(-9)
 
 
 def test_compute_calls_fail_closed_without_launching():
@@ -95,7 +106,7 @@ def test_compute_calls_fail_closed_without_launching():
     assert L.skv_attention_decode_paged(None, ctypes.byref(a), None) == -1
     d.head_dim = 100
     assert L.skv_attention_decode(ctypes.byref(d), ctypes.byref(a), None) == -2
-    for s in (0, -3, 1, -4, -8, 99):
+    for s in (0, -3, 1, -4, -8, -9, 99):
         assert isinstance(skv.status_str(s), str) and skv.status_str(s)
 
 
