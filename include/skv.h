@@ -105,7 +105,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 1
+#define SKV_ABI_VERSION 2
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
 
@@ -281,6 +281,20 @@ int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int
                         const int32_t* plan_meta, const skv_partials* p, void* stream);
 int skv_splitkv_combine(const skv_desc* d, const skv_args* a, int32_t num_splits,
                         const int32_t* plan_meta, const skv_partials* p, void* stream);
+
+/* ---- single-kernel split + merge ([DR] points for reviewer decision, Q1) ----
+ * The partial stage alone, arguments as skv_splitkv_partial, where the last
+ * workgroup to finish among those of a (request, KV head) also merges that
+ * pair's records into o, in increasing split order with the arithmetic of
+ * skv_splitkv_combine: o is bit-identical to the two-stage call, whichever
+ * workgroup arrives last.
+ * counters: DEVICE int32 [B * Hkv], all zero before the first call; each
+ * call leaves them zero again, so the call can be captured and replayed.
+ * Calls that overlap in time on one counters buffer race and are not
+ * allowed; a call that fails validation touches nothing. SKV_ERR_NULL when
+ * counters is NULL. */
+int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
+                      const int32_t* plan_meta, const skv_partials* p, int32_t* counters, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

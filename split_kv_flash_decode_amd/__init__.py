@@ -95,6 +95,8 @@ EXPORTS = {
                                            _c_ptr, ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_combine": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32,
                                            _c_ptr, ctypes.POINTER(Partials), _c_ptr]),
+    "skv_splitkv_fused": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_i32,
+                                         _c_ptr, ctypes.POINTER(Partials), _c_ptr, _c_ptr]),
 }
 
 _LIB = None
@@ -296,6 +298,18 @@ def splitkv_combine(desc: Desc, args: Args, num_splits: int, ws: Workspace,
     _check(lib().skv_splitkv_combine(ctypes.byref(desc), ctypes.byref(args), int(num_splits),
                                      _ptr(plan_meta_dev), ctypes.byref(ws.struct), _stream(stream)),
            "skv_splitkv_combine")
+
+
+def splitkv_fused(desc: Desc, args: Args, paged: bool, num_splits: int, ws: Workspace,
+                  counters: torch.Tensor, plan_meta_dev: Optional[torch.Tensor] = None, stream=None):
+    """Single-kernel split + merge: ``counters`` is a zeroed int32 device tensor
+    of at least B * Hkv entries (left zero after the call)."""
+    if counters.dtype != torch.int32 or not counters.is_cuda or counters.numel() < desc.batch * desc.num_kv_heads:
+        raise ValueError("counters: int32 device tensor of B * Hkv entries expected")
+    _check(lib().skv_splitkv_fused(ctypes.byref(desc), ctypes.byref(args), int(paged), int(num_splits),
+                                   _ptr(plan_meta_dev), ctypes.byref(ws.struct), _ptr(counters),
+                                   _stream(stream)),
+           "skv_splitkv_fused")
 
 
 def plan_meta_len(batch: int, capacity: int) -> int:

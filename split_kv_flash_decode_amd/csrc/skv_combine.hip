@@ -36,43 +36,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
   }
   int j, h;
   row_jh(p, g, r, &j, &h);
-
-  float M = -INFINITY;
-  bool any = false;
-  for (int s = 0; s < S; ++s) {
-    const int64_t rec = ((int64_t)(slot0 + s) * p.Hkv + g) * p.rho + r;
-    if (p.pl[rec] > 0.0f) {
-      M = fmaxf(M, p.pm[rec]);
-      any = true;
-    }
-  }
-  floatx4 out = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (any) {
-    const float s2 = p.has_sink ? p.sinks[h] * kLog2e : 0.0f;
-    if (p.has_sink) M = fmaxf(M, s2);
-    float L = 0.0f;
-    floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < S; ++s) {
-      const int64_t rec = ((int64_t)(slot0 + s) * p.Hkv + g) * p.rho + r;
-      const float l = p.pl[rec];
-      if (l > 0.0f) {
-        const float w = fexp2(p.pm[rec] - M);
-        const floatx4 acc = *reinterpret_cast<const floatx4*>(p.pacc + rec * p.D + d);
-        L += w * l;
-        a[0] += w * acc[0];
-        a[1] += w * acc[1];
-        a[2] += w * acc[2];
-        a[3] += w * acc[3];
-      }
-    }
-    if (p.has_sink) L += fexp2(s2 - M);
-    const float inv = 1.0f / (L + 1e-9f);
-    out[0] = a[0] * inv;
-    out[1] = a[1] * inv;
-    out[2] = a[2] * inv;
-    out[3] = a[3] * inv;
-  }
-  store_o4(p, qo_idx(p, b, j, h, d), out);
+  store_o4(p, qo_idx(p, b, j, h, d), merge_splits4(p, g, r, d, h, S, slot0));
 }
 
 int launch_combine(Params p, void* stream) {

@@ -156,4 +156,107 @@ __device__ __forceinline__ void row_jh(const Params& p, int g, int r, int* j, in
   *h = g * p.G + (r - (r / p.G) * p.G);
 }
 
+// Merged output of query row r, d .. d + 3, of request b and KV head g from
+// the records of its S splits (slots slot0 .. slot0 + S - 1), visited in
+// increasing split order: the flash-decoding merge (tiny-llm #11 split-KV
+// design record, "Design"); h is the row's query head (for its sink).
+__device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, int d, int h, int S, int slot0) {
+  // Every split of the request has a record (an empty one: m = -inf, l = 0,
+  // acc = 0). The splits are read in batches of 16 whose loads are all in
+  // flight together (indices past S re-read split S - 1 and take weight 0);
+  // records with weight 0 add exact zeros, so the sums are bit-identical to
+  // visiting the non-empty records one by one in increasing s.
+  constexpr int NB = 16;
+  const int64_t rs = (int64_t)p.Hkv * p.rho;       // record stride between splits
+  const int64_t rec0 = (int64_t)slot0 * rs + (int64_t)g * p.rho + r;
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    float lb[NB], mb[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = s0 + i < S ? s0 + i : S - 1;
+      lb[i] = p.pl[rec0 + s * rs];
+      mb[i] = p.pm[rec0 + s * rs];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) M = (s0 + i < S && lb[i] > 0.0f) ? fmaxf(M, mb[i]) : M;
+  }
+  floatx4 out = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (M != -INFINITY) {
+    const float s2 = p.has_sink ? p.sinks[h] * kLog2e : 0.0f;
+    if (p.has_sink) M = fmaxf(M, s2);
+    float L = 0.0f;
+    floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      float lb[NB], mb[NB];
+      floatx4 ab[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int s = s0 + i < S ? s0 + i : S - 1;
+        lb[i] = p.pl[rec0 + s * rs];
+        mb[i] = p.pm[rec0 + s * rs];
+        ab[i] = *reinterpret_cast<const floatx4*>(p.pacc + (rec0 + s * rs) * p.D + d);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const float w = (s0 + i < S && lb[i] > 0.0f) ? fexp2(mb[i] - M) : 0.0f;
+        L += w * lb[i];
+        a[0] += w * ab[i][0];
+        a[1] += w * ab[i][1];
+        a[2] += w * ab[i][2];
+        a[3] += w * ab[i][3];
+      }
+    }
+    if (p.has_sink) L += fexp2(s2 - M);
+    const float inv = 1.0f / (L + 1e-9f);
+    out[0] = a[0] * inv;
+    out[1] = a[1] * inv;
+    out[2] = a[2] * inv;
+    out[3] = a[3] * inv;
+  }
+  return out;
+}
+
+// Single-kernel split + merge (tiny-llm #11 split-KV design record, points
+// for reviewer decision, Q1): called by every workgroup of a partial kernel
+// after it wrote its records. The workgroups of one (request, KV head) count
+// themselves on a device-scope counter; the last one to arrive merges all of
+// that pair's rows in fixed split order (so the output does not depend on
+// which workgroup was last) and resets the counter to zero for the next call.
+// One agent-scope release fence per workgroup before it counts (after a
+// barrier, so it covers every wave's stores), an acquire fence in the merging
+// workgroup after: the records of workgroups on other XCDs are then visible
+// to it.
+__device__ __forceinline__ void fused_merge_tail(const Params& p, int b, int g, int nthreads) {
+  __shared__ int last_s;
+  const int tid = threadIdx.x;
+  int S, slot0;
+  if (p.plan) {
+    S = p.plan[4 + b];
+    slot0 = p.plan[4 + p.B + b];
+  } else {
+    S = p.num_splits;
+    slot0 = b * S;
+  }
+  __syncthreads();                                 // the workgroup's record stores are done
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and visible device-wide
+    int* cnt = p.counters + (int64_t)b * p.Hkv + g;
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == S * p.row_groups - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = last;
+  }
+  __syncthreads();
+  if (!last_s) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int tpr = p.D >> 2;                        // four d per thread
+  for (int idx = tid; idx < p.rho * tpr; idx += nthreads) {
+    const int r = idx / tpr, d = 4 * (idx - r * tpr);
+    int j, h;
+    row_jh(p, g, r, &j, &h);
+    store_o4(p, qo_idx(p, b, j, h, d), merge_splits4(p, g, r, d, h, S, slot0));
+  }
+}
+
 }  // namespace skv

@@ -461,6 +461,30 @@ int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int
   return run_partial(prm, stream);
 }
 
+int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
+                      const int32_t* plan_meta, const skv_partials* p, int32_t* counters, void* stream) {
+  int rc = check_desc(d, paged);
+  if (rc) return rc;
+  rc = check_args(d, a, paged);
+  if (rc) return rc;
+  if (!counters) return SKV_ERR_NULL;
+  int64_t slots;
+  if (plan_meta) {
+    if (!paged) return SKV_ERR_UNSUPPORTED;
+    if (num_splits < d->batch) return SKV_ERR_CAPACITY;
+    slots = (int64_t)num_splits * d->num_kv_heads;
+  } else {
+    if (num_splits < 1 || num_splits > SKV_MAX_SPLITS) return SKV_ERR_SPLITS;
+    slots = skv_uniform_slots(d, num_splits);
+  }
+  if (slots * 64 > INT32_MAX) return SKV_ERR_SHAPE;
+  rc = check_partials(d, p, slots);
+  if (rc) return rc;
+  skv::Params prm = make_params(d, a, paged, num_splits, plan_meta, p, 0);
+  prm.counters = counters;
+  return run_partial(prm, stream);
+}
+
 int skv_splitkv_combine(const skv_desc* d, const skv_args* a, int32_t num_splits,
                         const int32_t* plan_meta, const skv_partials* p, void* stream) {
   int rc = check_desc(d, -1);

@@ -24,6 +24,7 @@ struct Params {
   float* pl;
   float* pacc;
   const int32_t* plan;   // device plan metadata, or nullptr for uniform splits
+  int32_t* counters;     // single-kernel merge: arrival counters [B * Hkv], or nullptr
   int32_t B, R, Hq, Hkv, D, G, rho;
   int32_t causal, window;
   float scale_log2;      // scale * log2(e)

@@ -893,6 +893,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         p.pl[rec] = fin_s[rr][1];
       }
     }
+    if (p.counters) fused_merge_tail(p, b, g, NT);
   }
 }
 

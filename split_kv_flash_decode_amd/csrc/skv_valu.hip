@@ -235,6 +235,7 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
 #pragma unroll
       for (int k = 0; k < DPL; ++k) p.pacc[rec * D + lane + 64 * k] = acc[rr][k];
     }
+    if (p.counters) fused_merge_tail(p, b, g, 64);
   }
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), f"{n} missing from libskv.so"
     assert set(names) == set(skv.EXPORTS), "binding and header disagree"
-    assert skv.abi_version() == 1
+    assert skv.abi_version() == 2
 
 
 def _desc(**kw):
