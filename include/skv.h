@@ -107,6 +107,7 @@ extern "C" {
 
 #define SKV_ABI_VERSION 2
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
+#define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
 
 /* Status codes. */
@@ -265,6 +266,17 @@ int skv_plan_capacity(const skv_plan_hints* h, const int32_t* host_ctx, int32_t*
  * int32 for capacity C from host context lengths. info may be NULL. */
 int skv_plan_fill(const skv_plan_hints* h, const int32_t* host_ctx, int32_t capacity_items,
                   int32_t* meta, int64_t meta_len, skv_plan_info* info);
+
+/* Device-side refresh ([PA] intro, Changes; graph replay with changing
+ * lengths): fill the DEVICE metadata block `meta_dev` (meta_len int32, for
+ * capacity C) from the DEVICE context lengths `ctx_dev` [B] with one kernel
+ * on `stream`; the block is bit-identical to what skv_plan_fill writes for
+ * the same lengths. Nothing is copied to the host, so a captured step
+ * (refresh, then the planned call) re-plans on every replay. Host checks as
+ * skv_plan_fill; B <= SKV_PLAN_DEVICE_MAX_BATCH (SKV_ERR_UNSUPPORTED
+ * otherwise). */
+int skv_plan_refresh_device(const skv_plan_hints* h, const int32_t* ctx_dev, int32_t capacity_items,
+                            int32_t* meta_dev, int64_t meta_len, void* stream);
 
 /* Paged split-KV over a plan: plan_meta is the DEVICE copy of the block,
  * capacity_items its C (the grid size), partials hold C * Hkv records. */

@@ -97,6 +97,8 @@ EXPORTS = {
                                            _c_ptr, ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_fused": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_i32,
                                          _c_ptr, ctypes.POINTER(Partials), _c_ptr, _c_ptr]),
+    "skv_plan_refresh_device": (ctypes.c_int, [ctypes.POINTER(PlanHints), _c_ptr, _c_i32, _c_ptr,
+                                               ctypes.c_int64, _c_ptr]),
 }
 
 _LIB = None
@@ -353,6 +355,17 @@ def plan_fill(hints: PlanHints, host_ctx, capacity: int, meta: torch.Tensor) -> 
     return info
 
 
+def plan_refresh_device(hints: PlanHints, ctx_dev: torch.Tensor, capacity: int, meta_dev: torch.Tensor,
+                        stream=None) -> None:
+    """Re-plan on the GPU from device context lengths into the device block
+    ``meta_dev`` (bit-identical to plan_fill for the same lengths)."""
+    if ctx_dev.dtype != torch.int32 or meta_dev.dtype != torch.int32 or not (ctx_dev.is_cuda and meta_dev.is_cuda):
+        raise ValueError("ctx_dev and meta_dev: int32 device tensors expected")
+    _check(lib().skv_plan_refresh_device(ctypes.byref(hints), _ptr(ctx_dev), int(capacity), _ptr(meta_dev),
+                                         int(meta_dev.numel()), _stream(stream)),
+           "skv_plan_refresh_device")
+
+
 class Plan:
     """A plan's fixed-capacity metadata: pinned host copies and one device copy.
 
@@ -385,3 +398,8 @@ class Plan:
             ev.record(s)
         self.events[i] = ev
         return self.info
+
+    def refresh_device(self, ctx_dev: torch.Tensor, stream=None) -> None:
+        """Re-plan on the GPU from the device lengths (capturable; ``info``
+        keeps the last host-side values)."""
+        plan_refresh_device(self.hints, ctx_dev, self.capacity, self.dev, stream)

@@ -461,6 +461,31 @@ int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int
   return run_partial(prm, stream);
 }
 
+int skv_plan_refresh_device(const skv_plan_hints* h, const int32_t* ctx_dev, int32_t capacity_items,
+                            int32_t* meta_dev, int64_t meta_len, void* stream) {
+  int rc = check_hints(h);
+  if (rc) return rc;
+  if (!ctx_dev || !meta_dev) return SKV_ERR_NULL;
+  Hints r = resolve(h);
+  if (r.B > SKV_PLAN_DEVICE_MAX_BATCH) return SKV_ERR_UNSUPPORTED;
+  if (capacity_items < r.B) return SKV_ERR_CAPACITY;
+  if (meta_len < skv_plan_meta_len(r.B, capacity_items)) return SKV_ERR_PLAN;
+  skv::PlanDev d;
+  d.B = r.B;
+  d.R = r.R;
+  d.Hkv = r.Hkv;
+  d.causal = r.causal;
+  d.window = r.window;
+  d.cus = r.cus;
+  d.ctas = r.ctas;
+  d.explicit_p = r.explicit_p;
+  d.maxp = r.maxp;
+  d.work = r.work;
+  d.min_tokens = r.min_tokens;
+  d.C = capacity_items;
+  return skv::launch_plan_device(d, ctx_dev, meta_dev, stream);
+}
+
 int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
                       const int32_t* plan_meta, const skv_partials* p, int32_t* counters, void* stream) {
   int rc = check_desc(d, paged);

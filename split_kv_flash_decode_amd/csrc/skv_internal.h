@@ -41,6 +41,11 @@ struct Params {
   int32_t q_dtype, kv_dtype, v_layout, block_size, impl;
 };
 
+// Resolved planner hints for the device-side planner.
+struct PlanDev {
+  int32_t B, R, Hkv, causal, window, cus, ctas, explicit_p, maxp, work, min_tokens, C;
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSplitAlign = SKV_SPLIT_ALIGN;
 // Lazy rescaling: the running reference maximum is only raised when a new
@@ -58,12 +63,9 @@ constexpr float kRescaleSlack = 8.0f;
 // Split s of S over the visible union of a request of length ctx:
 // [u, ctx) with u = 0 or the earliest row's window start aligned down;
 // chunk = ceil((ctx - u) / S) rounded up to kSplitAlign.
-SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, int* lo, int* hi) {
-  if (ctx <= 0) {
-    *lo = 0;
-    *hi = 0;
-    return;
-  }
+// Start u of the visible union and chunk length of S splits of a request of
+// length ctx > 0.
+SKV_HD void split_geometry(int ctx, int R, int causal, int window, int S, int* u_out, int* chunk_out) {
   int u = 0;
   if (window > 0) {
     int pmin = causal ? ctx - R : ctx - 1;
@@ -74,6 +76,18 @@ SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, in
   int span = ctx - u;
   int chunk = (span + S - 1) / S;
   chunk = ((chunk + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
+  *u_out = u;
+  *chunk_out = chunk;
+}
+
+SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, int* lo, int* hi) {
+  if (ctx <= 0) {
+    *lo = 0;
+    *hi = 0;
+    return;
+  }
+  int u, chunk;
+  split_geometry(ctx, R, causal, window, S, &u, &chunk);
   long long l0 = (long long)u + (long long)s * chunk;
   if (l0 >= ctx) {
     *lo = ctx;
@@ -127,5 +141,6 @@ namespace skv {
 int launch_partial_valu(Params p, void* stream);
 int launch_partial_mfma(Params p, void* stream);
 int launch_combine(Params p, void* stream);
+int launch_plan_device(const PlanDev& h, const int32_t* ctx, int32_t* meta, void* stream);
 bool mfma_supported(const Params& p);
 }  // namespace skv

@@ -206,3 +206,20 @@ def test_refresh_keeps_capacity():
     assert C == cap and n <= cap and info.num_items == n
     with pytest.raises(skv.SkvError):
         skv.plan_fill(h, [1000] * 8, 7, torch.zeros(skv.plan_meta_len(8, 7), dtype=torch.int32))
+
+
+def test_device_plan_refresh_fails_closed_on_the_host():
+    """Host checks of skv_plan_refresh_device run before any HIP call."""
+    L = skv.lib()
+    h = skv.plan_hints(4, 1, 1)
+    fake = ctypes.c_void_p(4096)
+    n = skv.plan_meta_len(4, 8)
+    assert L.skv_plan_refresh_device(ctypes.byref(h), None, 8, fake, n, None) == -1
+    assert L.skv_plan_refresh_device(ctypes.byref(h), fake, 8, None, n, None) == -1
+    assert L.skv_plan_refresh_device(ctypes.byref(h), fake, 3, fake, n, None) == -5   # capacity < B
+    assert L.skv_plan_refresh_device(ctypes.byref(h), fake, 8, fake, n - 1, None) == -8
+    big = skv.plan_hints(4097, 1, 1)
+    assert L.skv_plan_refresh_device(ctypes.byref(big), fake, 8192, fake,
+                                     skv.plan_meta_len(4097, 8192), None) == -6
+    bad = skv.plan_hints(4, 0, 1)
+    assert L.skv_plan_refresh_device(ctypes.byref(bad), fake, 8, fake, n, None) == -8
