@@ -109,6 +109,12 @@ extern "C" {
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
 #define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
+/* The planner's default cap on partitions per request (max_partitions = 0):
+ * a merge visits every record of a request, so past this many partitions
+ * the merge costs more than the extra partial workgroups save (measured on
+ * one 200,000-key request with fifteen of 1,024). An explicit
+ * max_partitions up to SKV_MAX_SPLITS still applies. */
+#define SKV_PLAN_DEFAULT_MAX_PARTITIONS 128
 
 /* Status codes. */
 #define SKV_OK 0
@@ -240,7 +246,7 @@ typedef struct skv_plan_hints {
   int32_t num_cus;                 /* 0 = 256 */
   int32_t ctas_per_cu;             /* base occupancy budget per CU, 0 = 2 */
   int32_t partitions_per_request;  /* > 0: explicit P_b for every request (precedence) */
-  int32_t max_partitions;          /* cap on P_b, 0 = SKV_MAX_SPLITS */
+  int32_t max_partitions;          /* cap on P_b, 0 = SKV_PLAN_DEFAULT_MAX_PARTITIONS */
   int32_t work_per_partition;      /* target key-rows (keys * R) per partition, 0 = 50000 */
   int32_t min_tokens_per_partition;/* 0 = 256 */
   int32_t reserved;

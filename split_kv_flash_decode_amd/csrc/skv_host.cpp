@@ -156,7 +156,7 @@ Hints resolve(const skv_plan_hints* h) {
   r.cus = h->num_cus > 0 ? h->num_cus : 256;
   r.ctas = h->ctas_per_cu > 0 ? h->ctas_per_cu : 2;
   r.explicit_p = h->partitions_per_request;
-  r.maxp = h->max_partitions > 0 ? std::min(h->max_partitions, SKV_MAX_SPLITS) : SKV_MAX_SPLITS;
+  r.maxp = h->max_partitions > 0 ? std::min(h->max_partitions, SKV_MAX_SPLITS) : SKV_PLAN_DEFAULT_MAX_PARTITIONS;
   r.work = h->work_per_partition > 0 ? h->work_per_partition : 50000;
   r.min_tokens = h->min_tokens_per_partition > 0 ? h->min_tokens_per_partition : 256;
   return r;
