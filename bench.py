@@ -135,57 +135,32 @@ def cpu_baseline(problem, spec, budget_s: float = 12.0, max_requests: int = 200)
     }
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--block-size", type=int, default=0)
-    ap.add_argument("--v-layout", default="")
-    ap.add_argument("--seed", type=int, default=4)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run 1 GiB device-to-device copies (counter calibration)")
-    args = ap.parse_args(argv)
+# Rows of the Performance table of aiter #5628 "tune MTP work budgets and
+# planned reduction" (another implementation on the same GPU model; context,
+# not the target): contexts, page size, V layout, the page's time per step in
+# microseconds and its effective TB/s.
+PAGE_TABLE = [
+    ("B200, all 200000", 4, {}, 16, "plain", 2295.66, 4.607),
+    ("B200, all 200000", 4, {}, 16, "transposed", 2332.80, 4.534),
+    ("B200, all 200000", 4, {}, 128, "plain", 2325.20, 4.545),
+    ("B200, all 200000", 4, {}, 128, "transposed", 2459.28, 4.297),
+    ("B16, one 100000 + fifteen 1024", 5, {"ctx": (100000,) + (1024,) * 15}, 128, "transposed", 48.93, 0.633),
+    ("B16, one 200000 + fifteen 1024", 5, {"ctx": (200000,) + (1024,) * 15}, 128, "transposed", 57.50, 0.998),
+]
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path needs no collectives; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
-        return 2
 
+def timed_steps(spec, seed: int, steps: int, warmup: int):
+    """Generate the workload, run the planned step (host plan refresh, metadata
+    copy, partial, combine) ``warmup`` + ``steps`` times; returns
+    (ms per step, partial ms list, combine ms list, plan)."""
     import torch
 
     import split_kv_flash_decode_amd as skv
-    from skvgen import config_spec, make_problem
+    from skvgen import make_problem
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.calibrate_copy:
-        # A plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of these
-        # dispatches give the counter-to-bytes factor used for ``traffic``.
-        n = 1 << 28                                     # 2^28 fp32 = 1 GiB
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": 4 * n, "copies": 3}), flush=True)
-        return 0
-    overrides = {}
-    if args.block_size:
-        overrides["block_size"] = args.block_size
-    if args.v_layout:
-        overrides["v_layout"] = args.v_layout
-    spec = config_spec(args.config, **overrides)
     dev = torch.device("cuda:0")
-    print(f"[bench] generating {spec.name} on {dev} ...", file=sys.stderr, flush=True)
-    t = time.time()
-    p = make_problem(spec, seed=args.seed, device=dev)
+    p = make_problem(spec, seed=seed, device=dev)
     torch.cuda.synchronize()
-    print(f"[bench] inputs ready in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
-
     o = torch.empty_like(p.q)
     d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
                       window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
@@ -209,19 +184,95 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     part_ms = [e[0].elapsed_time(e[1]) for e in events]
     comb_ms = [e[1].elapsed_time(e[2]) for e in events]
-    ms_per_step = wall * 1e3 / args.steps
+    return wall * 1e3 / steps, part_ms, comb_ms, plan, p
+
+
+def table(args) -> int:
+    import torch
+
+    from skvgen import config_spec
+
+    for name, n, over, bs, vl, page_us, page_tbs in PAGE_TABLE:
+        spec = config_spec(n, block_size=bs, v_layout=vl, **over)
+        small = max(spec.ctx) * spec.B < 10_000_000
+        steps, warmup = (400, 50) if small else (args.steps, args.warmup)
+        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup)
+        tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
+        print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
+                          "effective_TBps": round(tbs, 3), "page_us_per_step": page_us,
+                          "page_TBps": page_tbs, "time_vs_page": round(ms * 1e3 / page_us, 4),
+                          "partial_us_mean": round(sum(part_ms) / len(part_ms) * 1e3, 2),
+                          "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+                          "plan_items": plan.info.num_items, "steps": steps, "warmup": warmup}), flush=True)
+        del p
+        torch.cuda.empty_cache()
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--block-size", type=int, default=0)
+    ap.add_argument("--v-layout", default="")
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 1 GiB device-to-device copies (counter calibration)")
+    ap.add_argument("--table", action="store_true",
+                    help="time the six rows of the planned-reduction page's Performance table "
+                         "(one JSON line per row, with the page's own time beside ours)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path needs no collectives; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from skvgen import config_spec
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        # A plain copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE of these
+        # dispatches give the counter-to-bytes factor used for ``traffic``.
+        n = 1 << 28                                     # 2^28 fp32 = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 4 * n, "copies": 3}), flush=True)
+        return 0
+    if args.table:
+        return table(args)
+    overrides = {}
+    if args.block_size:
+        overrides["block_size"] = args.block_size
+    if args.v_layout:
+        overrides["v_layout"] = args.v_layout
+    spec = config_spec(args.config, **overrides)
+    print(f"[bench] generating {spec.name} on cuda:0 and timing ...", file=sys.stderr, flush=True)
+    t = time.time()
+    ms_per_step, part_ms, comb_ms, plan, p = timed_steps(spec, args.seed, args.steps, args.warmup)
+    print(f"[bench] done in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     nbytes = spec_bytes(spec)
     tbs = nbytes / (ms_per_step * 1e-3) / 1e12
 

@@ -379,7 +379,8 @@ class Plan:
         self.capacity = capacity if capacity is not None else plan_capacity(hints, host_ctx)
         n = plan_meta_len(hints.batch, self.capacity)
         self.host = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(2)]
-        self.events = [None, None]
+        self.events = [torch.cuda.Event(), torch.cuda.Event()]
+        self.used = [False, False]
         self.dev = torch.empty(n, dtype=torch.int32, device=device)
         self.turn = 0
         self.info = None
@@ -388,15 +389,17 @@ class Plan:
     def refresh(self, host_ctx, stream=None):
         i = self.turn
         self.turn ^= 1
-        if self.events[i] is not None:
-            self.events[i].synchronize()
+        if self.used[i]:
+            self.events[i].synchronize()           # its previous copy has completed
         self.info = plan_fill(self.hints, host_ctx, self.capacity, self.host[i])
         s = torch.cuda.current_stream() if stream is None else stream
-        with torch.cuda.stream(s):
+        if stream is None:
             self.dev.copy_(self.host[i], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(s)
-        self.events[i] = ev
+        else:
+            with torch.cuda.stream(s):
+                self.dev.copy_(self.host[i], non_blocking=True)
+        self.events[i].record(s)
+        self.used[i] = True
         return self.info
 
     def refresh_device(self, ctx_dev: torch.Tensor, stream=None) -> None:

@@ -160,54 +160,108 @@ __device__ __forceinline__ void row_jh(const Params& p, int g, int r, int* j, in
 // the records of its S splits (slots slot0 .. slot0 + S - 1), visited in
 // increasing split order: the flash-decoding merge (tiny-llm #11 split-KV
 // design record, "Design"); h is the row's query head (for its sink).
-__device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, int d, int h, int S, int slot0) {
-  // Every split of the request has a record (an empty one: m = -inf, l = 0,
-  // acc = 0). The splits are read in batches of 16 whose loads are all in
-  // flight together (indices past S re-read split S - 1 and take weight 0);
-  // records with weight 0 add exact zeros, so the sums are bit-identical to
-  // visiting the non-empty records one by one in increasing s.
-  constexpr int NB = 16;
-  const int64_t rs = (int64_t)p.Hkv * p.rho;       // record stride between splits
-  const int64_t rec0 = (int64_t)slot0 * rs + (int64_t)g * p.rho + r;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += NB) {
+// x of lane K of this lane's group of four (DPP quad_perm [K, K, K, K]).
+template <int K>
+__device__ __forceinline__ float quad_lane(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xF, 0xF, true));
+}
+
+// Running state of a split merge: maximum M, sum L and accumulators a (for
+// four d), all relative to M.
+struct MergeState {
+  float M, L;
+  floatx4 a;
+};
+
+// Take one record (m, l, acc) into the running state: a record that raises
+// the maximum rescales the sums first; empty records (l = 0) are skipped.
+__device__ __forceinline__ void merge_absorb(MergeState& t, float m, float l, floatx4 acc) {
+  if (!(l > 0.0f)) return;
+  if (m > t.M) {
+    const float sc = fexp2(t.M - m);                // 0 while M is -inf
+    t.L *= sc;
+    t.a[0] *= sc;
+    t.a[1] *= sc;
+    t.a[2] *= sc;
+    t.a[3] *= sc;
+    t.M = m;
+  }
+  const float w = fexp2(m - t.M);
+  t.L += w * l;
+  t.a[0] += w * acc[0];
+  t.a[1] += w * acc[1];
+  t.a[2] += w * acc[2];
+  t.a[3] += w * acc[3];
+}
+
+// Records of splits [s_begin, s_end) in increasing order, read in batches of
+// NB whose loads are all in flight together (indices past the range re-read
+// its last split and are skipped).
+template <int NB>
+__device__ __forceinline__ MergeState merge_range(const Params& p, int64_t rec0, int64_t rs, int d, int s_begin,
+                                                  int s_end) {
+  MergeState t{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int s0 = s_begin; s0 < s_end; s0 += NB) {
     float lb[NB], mb[NB];
+    floatx4 ab[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int s = s0 + i < S ? s0 + i : S - 1;
+      const int s = s0 + i < s_end ? s0 + i : s_end - 1;
       lb[i] = p.pl[rec0 + s * rs];
       mb[i] = p.pm[rec0 + s * rs];
+      ab[i] = *reinterpret_cast<const floatx4*>(p.pacc + (rec0 + s * rs) * p.D + d);
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) M = (s0 + i < S && lb[i] > 0.0f) ? fmaxf(M, mb[i]) : M;
+    for (int i = 0; i < NB; ++i)
+      if (s0 + i < s_end) merge_absorb(t, mb[i], lb[i], ab[i]);
   }
+  return t;
+}
+
+// Merged output of query row r, d .. d + 3, of request b and KV head g from
+// the records of its S splits (slots slot0 .. slot0 + S - 1): the
+// flash-decoding merge (tiny-llm #11 split-KV design record, "Design"); h is
+// the row's query head (for its sink). Called by four adjacent lanes q = 0..3
+// together: lane q merges its quarter of the splits, then every lane takes
+// the four quarter states in order q = 0..3 (with the same step as single
+// records), so the order is fixed and the result deterministic. With at most
+// four splits every quarter holds at most one record and the sequence is the
+// per-record one; with one split the operations are those of the single-pass
+// finalize (finalize_one), so S = 1 stays bit-identical to the single pass.
+__device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, int d, int h, int S, int slot0,
+                                                 int q) {
+  const int64_t rs = (int64_t)p.Hkv * p.rho;       // record stride between splits
+  const int64_t rec0 = (int64_t)slot0 * rs + (int64_t)g * p.rho + r;
+  const int c = (S + 3) >> 2;
+  const int sb = q * c < S ? q * c : S, se = (q + 1) * c < S ? (q + 1) * c : S;
+  // (batch size from the quarter length, the same for every lane of a
+  // request: no loads wasted on short quarters; batches of at most eight
+  // keep the register count, and so the occupancy, up)
+  const MergeState part = c <= 4 ? merge_range<4>(p, rec0, rs, d, sb, se) : merge_range<8>(p, rec0, rs, d, sb, se);
+  MergeState t{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
+  merge_absorb(t, quad_lane<0>(part.M), quad_lane<0>(part.L),
+               floatx4{quad_lane<0>(part.a[0]), quad_lane<0>(part.a[1]), quad_lane<0>(part.a[2]), quad_lane<0>(part.a[3])});
+  merge_absorb(t, quad_lane<1>(part.M), quad_lane<1>(part.L),
+               floatx4{quad_lane<1>(part.a[0]), quad_lane<1>(part.a[1]), quad_lane<1>(part.a[2]), quad_lane<1>(part.a[3])});
+  merge_absorb(t, quad_lane<2>(part.M), quad_lane<2>(part.L),
+               floatx4{quad_lane<2>(part.a[0]), quad_lane<2>(part.a[1]), quad_lane<2>(part.a[2]), quad_lane<2>(part.a[3])});
+  merge_absorb(t, quad_lane<3>(part.M), quad_lane<3>(part.L),
+               floatx4{quad_lane<3>(part.a[0]), quad_lane<3>(part.a[1]), quad_lane<3>(part.a[2]), quad_lane<3>(part.a[3])});
   floatx4 out = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (M != -INFINITY) {
-    const float s2 = p.has_sink ? p.sinks[h] * kLog2e : 0.0f;
-    if (p.has_sink) M = fmaxf(M, s2);
-    float L = 0.0f;
-    floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < S; s0 += NB) {
-      float lb[NB], mb[NB];
-      floatx4 ab[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int s = s0 + i < S ? s0 + i : S - 1;
-        lb[i] = p.pl[rec0 + s * rs];
-        mb[i] = p.pm[rec0 + s * rs];
-        ab[i] = *reinterpret_cast<const floatx4*>(p.pacc + (rec0 + s * rs) * p.D + d);
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const float w = (s0 + i < S && lb[i] > 0.0f) ? fexp2(mb[i] - M) : 0.0f;
-        L += w * lb[i];
-        a[0] += w * ab[i][0];
-        a[1] += w * ab[i][1];
-        a[2] += w * ab[i][2];
-        a[3] += w * ab[i][3];
-      }
+  if (t.M != -INFINITY) {
+    float L = t.L;
+    floatx4 a = t.a;
+    if (p.has_sink) {
+      const float s2 = p.sinks[h] * kLog2e;
+      const float M2 = fmaxf(t.M, s2);
+      const float sc = fexp2(t.M - M2);
+      L *= sc;
+      a[0] *= sc;
+      a[1] *= sc;
+      a[2] *= sc;
+      a[3] *= sc;
+      L += fexp2(s2 - M2);
     }
-    if (p.has_sink) L += fexp2(s2 - M);
     const float inv = 1.0f / (L + 1e-9f);
     out[0] = a[0] * inv;
     out[1] = a[1] * inv;
@@ -250,12 +304,14 @@ __device__ __forceinline__ void fused_merge_tail(const Params& p, int b, int g, 
   __syncthreads();
   if (!last_s) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int tpr = p.D >> 2;                        // four d per thread
-  for (int idx = tid; idx < p.rho * tpr; idx += nthreads) {
-    const int r = idx / tpr, d = 4 * (idx - r * tpr);
+  const int tpr = p.D >> 2;                        // four d per output, four lanes per output
+  for (int idx = tid; idx < 4 * p.rho * tpr; idx += nthreads) {
+    const int o = idx >> 2, q = idx & 3;
+    const int r = o / tpr, d = 4 * (o - r * tpr);
     int j, h;
     row_jh(p, g, r, &j, &h);
-    store_o4(p, qo_idx(p, b, j, h, d), merge_splits4(p, g, r, d, h, S, slot0));
+    const floatx4 v = merge_splits4(p, g, r, d, h, S, slot0, q);
+    if (q == 0) store_o4(p, qo_idx(p, b, j, h, d), v);
   }
 }
 
