@@ -57,7 +57,7 @@ def logical_bytes(ctx, *, R: int, Hq: int, Hkv: int, D: int, q_bytes: int, kv_by
     return qo + kv + sc + pt + 4 * B
 
 
-_DT = {"f32": 4, "bf16": 2, "int8": 1, "fp8": 1}
+_DT = {"f32": 4, "bf16": 2, "f16": 2, "int8": 1, "fp8": 1}
 
 
 def spec_bytes(spec) -> int:

@@ -132,7 +132,8 @@ typedef enum skv_dtype {
   SKV_F32 = 0,
   SKV_BF16 = 1,
   SKV_INT8 = 2,       /* KV only: symmetric int8 codes times an fp32 scale */
-  SKV_FP8_E4M3 = 3    /* KV only: OCP e4m3fn codes times an fp32 scale */
+  SKV_FP8_E4M3 = 3,   /* KV only: OCP e4m3fn codes times an fp32 scale */
+  SKV_F16 = 4         /* Q/O only: IEEE binary16 ([PA] Validation: FP16 coverage); O by RNE */
 } skv_dtype;
 
 typedef enum skv_v_layout { SKV_V_PLAIN = 0, SKV_V_TRANSPOSED = 1 } skv_v_layout;

@@ -25,7 +25,7 @@ closed forms, library routines and the pages' printed numbers; no function is
 "parity unpinned".
 """
 
-from .codecs import decode_bf16_bits, decode_fp8_e4m3fn, decode_storage, fp8_e4m3fn_table
+from .codecs import decode_bf16_bits, decode_f16_bits, decode_fp8_e4m3fn, decode_storage, fp8_e4m3fn_table
 from .attention import (
     SPLIT_ALIGN,
     combine_flash,
@@ -46,6 +46,7 @@ __all__ = [
     "decode_bf16_bits",
     "decode_fp8_e4m3fn",
     "decode_storage",
+    "decode_f16_bits",
     "fp8_e4m3fn_table",
     "gather_request",
     "row_positions",

@@ -3,6 +3,11 @@
 Test infrastructure only (see the package docstring).
 
 * bf16: the upper 16 bits of an IEEE-754 binary32; decoding is exact.
+* f16: IEEE-754 binary16, 1 sign bit, 5 exponent bits with bias 15, 10
+  mantissa bits; exponent field 0 encodes subnormals m/1024 * 2^-14, field 31
+  infinities (m = 0) and NaNs. Queries and outputs only (aiter #5628 "tune MTP
+  work budgets and planned reduction", Validation: the FP16 cases of the
+  decode tests).
 * int8: a two's-complement integer code; the value is the code itself, later
   multiplied by its fp32 scale (hipfire #760 "split packed-Q8 verifier KV
   scans", Summary: int8 "Q8" KV; the per-token-per-head scale is this
@@ -26,6 +31,18 @@ def decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     with np.errstate(invalid="ignore"):          # signalling-NaN patterns widen to NaN
         return u32.view(np.float32).astype(np.float64)
+
+
+def decode_f16_bits(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns (uint16) -> float64, exactly, from the field layout."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((u >> 15) & 1, -1.0, 1.0)
+    e = (u >> 10) & 0x1F
+    m = (u & 0x3FF).astype(np.float64)
+    normal = sign * (1.0 + m / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = sign * (m / 1024.0) * 2.0 ** (-14)
+    special = np.where(m == 0, sign * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 0x1F, special, normal))
 
 
 def _fp8_e4m3fn_scalar(code: int) -> float:
@@ -53,11 +70,13 @@ def decode_fp8_e4m3fn(codes: np.ndarray) -> np.ndarray:
 
 
 def decode_storage(arr: np.ndarray, dtype: str) -> np.ndarray:
-    """Decode a storage array of ``dtype`` ("f32", "bf16", "int8", "fp8") to float64."""
+    """Decode a storage array of ``dtype`` ("f32", "bf16", "f16", "int8", "fp8") to float64."""
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         return decode_bf16_bits(arr)
+    if dtype == "f16":
+        return decode_f16_bits(arr)
     if dtype == "int8":
         return np.asarray(arr, dtype=np.int8).astype(np.float64)
     if dtype == "fp8":

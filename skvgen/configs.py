@@ -39,7 +39,7 @@ class ProblemSpec:
     ctx: Tuple[int, ...]
     causal: bool
     window: int = 0
-    q_dtype: str = "bf16"          # "f32" | "bf16"  (O has the same dtype)
+    q_dtype: str = "bf16"          # "f32" | "bf16" | "f16"  (O has the same dtype)
     kv_dtype: str = "bf16"         # "f32" | "bf16" | "int8" | "fp8"
     block_size: int = 16
     v_layout: str = "plain"        # "plain" [bs][D] | "transposed" [D][bs]

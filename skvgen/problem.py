@@ -3,8 +3,8 @@
 Recipe (every draw from one ``torch.Generator`` seeded with ``seed``, on the
 device the problem is built on, in this order):
 
-1. Q ~ N(0, 1) * q_mult, shape [B][R][Hq][D], then stored as fp32 or bf16
-   (round-to-nearest-even cast).
+1. Q ~ N(0, 1) * q_mult, shape [B][R][Hq][D], then stored as fp32, bf16 or
+   fp16 (round-to-nearest-even cast).
 2. K pool values ~ N(0, 1), shape [P][Hkv][bs][D], drawn page chunk by page
    chunk; V pool values likewise.
 3. Storage encoding of K and V per (page, head, slot) row of D values:
@@ -49,7 +49,7 @@ _TORCH_STORAGE = {
 class Problem:
     spec: ProblemSpec
     paged: bool
-    q: torch.Tensor                    # [B][R][Hq][D] fp32 or bf16
+    q: torch.Tensor                    # [B][R][Hq][D] fp32, bf16 or fp16
     k: torch.Tensor                    # paged [P][Hkv][bs][D]; contiguous [B][Hkv][cap][D]
     v: torch.Tensor                    # plain as k; transposed [..][Hkv][D][bs or cap]
     k_scale: Optional[torch.Tensor]    # fp32 [P][Hkv][bs] or [B][Hkv][cap]
@@ -76,12 +76,12 @@ class Problem:
             sinks=mv(self.sinks))
 
     def host_arrays(self) -> dict:
-        """Storage as numpy arrays: bf16 as uint16 bit patterns, fp8 as uint8 codes."""
+        """Storage as numpy arrays: bf16 and fp16 as uint16 bit patterns, fp8 as uint8 codes."""
         def np_store(t):
             if t is None:
                 return None
             t = t.detach().cpu().contiguous()
-            if t.dtype == torch.bfloat16:
+            if t.dtype in (torch.bfloat16, torch.float16):
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
         return {name: np_store(getattr(self, name))
@@ -129,7 +129,8 @@ def make_problem(spec: ProblemSpec, seed: int, device="cpu", paged: bool = True,
     q = torch.randn((B, R, Hq, D), generator=g, device=dev, dtype=torch.float32)
     if spec.q_mult != 1.0:
         q.mul_(spec.q_mult)
-    q = q.to(torch.bfloat16) if spec.q_dtype == "bf16" else q
+    if spec.q_dtype in ("bf16", "f16"):
+        q = q.to(torch.bfloat16 if spec.q_dtype == "bf16" else torch.float16)
 
     pages_per_req = [-(-int(c) // bs) for c in spec.ctx]
     n_ref = sum(pages_per_req)

@@ -7,7 +7,7 @@ arithmetic runs in Python, and nothing falls back to a CPU path: if the
 library is missing, ``lib()`` raises.
 
 Storage conventions (the C header documents them in full):
-  q, o        [B][R][Hq][D] torch.float32 or torch.bfloat16 (o has q's dtype)
+  q, o        [B][R][Hq][D] torch.float32, torch.bfloat16 or torch.float16 (o has q's dtype)
   paged k     [pages][Hkv][block_size][D]; v the same ("plain") or
               [pages][Hkv][D][block_size] ("transposed")
   contiguous  k [B][Hkv][cap][D]; v [B][Hkv][cap][D] or [B][Hkv][D][cap]
@@ -28,7 +28,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libskv.so")
 
-SKV_F32, SKV_BF16, SKV_INT8, SKV_FP8_E4M3 = 0, 1, 2, 3
+SKV_F32, SKV_BF16, SKV_INT8, SKV_FP8_E4M3, SKV_F16 = 0, 1, 2, 3, 4
 SKV_V_PLAIN, SKV_V_TRANSPOSED = 0, 1
 SKV_IMPL_AUTO, SKV_IMPL_VALU, SKV_IMPL_MFMA = 0, 1, 2
 SKV_SPLIT_ALIGN = 64
@@ -137,7 +137,7 @@ def _check(rc: int, where: str):
 
 _KV_CODES = {torch.float32: SKV_F32, torch.bfloat16: SKV_BF16, torch.int8: SKV_INT8,
              torch.uint8: SKV_FP8_E4M3, torch.float8_e4m3fn: SKV_FP8_E4M3}
-_Q_CODES = {torch.float32: SKV_F32, torch.bfloat16: SKV_BF16}
+_Q_CODES = {torch.float32: SKV_F32, torch.bfloat16: SKV_BF16, torch.float16: SKV_F16}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

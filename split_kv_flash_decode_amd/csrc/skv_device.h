@@ -23,12 +23,24 @@ struct F32 {};
 struct BF16 {};
 struct I8 {};
 struct FP8 {};
+struct F16 {};   // Q/O only: IEEE binary16
 
 template <class T> struct Storage;
 template <> struct Storage<F32> { static constexpr int bytes = 4; static constexpr bool quant = false; };
 template <> struct Storage<BF16> { static constexpr int bytes = 2; static constexpr bool quant = false; };
 template <> struct Storage<I8> { static constexpr int bytes = 1; static constexpr bool quant = true; };
 template <> struct Storage<FP8> { static constexpr int bytes = 1; static constexpr bool quant = true; };
+template <> struct Storage<F16> { static constexpr int bytes = 2; static constexpr bool quant = false; };
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Round-to-nearest-even fp32 -> fp16 pair.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  floatx2 x = {a, b};
+  f16x2 y = __builtin_convertvector(x, f16x2);
+  return __builtin_bit_cast(uint32_t, y);
+}
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -51,6 +63,12 @@ __device__ __forceinline__ floatx2 fp8x2_to_f32(uint32_t w) {
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   bf16x2 y = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
   return __builtin_bit_cast(uint32_t, y);
 }
 
@@ -128,8 +146,8 @@ __device__ __forceinline__ float finalize_one(float m, float l, float acc, int h
 
 // Output element store: fp32 or bf16 (RNE).
 __device__ __forceinline__ void store_o1(const Params& p, int64_t idx, float x) {
-  if (p.q_dtype == SKV_BF16) {
-    uint32_t w = pack_bf16x2(x, 0.0f);
+  if (p.q_dtype == SKV_BF16 || p.q_dtype == SKV_F16) {
+    uint32_t w = p.q_dtype == SKV_BF16 ? pack_bf16x2(x, 0.0f) : pack_f16x2(x, 0.0f);
     reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)(w & 0xFFFF);
   } else {
     reinterpret_cast<float*>(p.o)[idx] = x;
@@ -139,6 +157,9 @@ __device__ __forceinline__ void store_o1(const Params& p, int64_t idx, float x) 
 __device__ __forceinline__ void store_o4(const Params& p, int64_t idx, floatx4 x) {
   if (p.q_dtype == SKV_BF16) {
     u32x2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + idx) = w;
+  } else if (p.q_dtype == SKV_F16) {
+    u32x2 w = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.o) + idx) = w;
   } else {
     *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(p.o) + idx) = x;

@@ -41,7 +41,7 @@ int check_desc(const skv_desc* d, int paged) {
   if (d->window < 0) return SKV_ERR_SHAPE;
   if (d->causal != 0 && d->causal != 1) return SKV_ERR_SHAPE;
   if (!(d->scale == d->scale) || isinf(d->scale)) return SKV_ERR_SHAPE;
-  if (d->q_dtype != SKV_F32 && d->q_dtype != SKV_BF16) return SKV_ERR_DTYPE;
+  if (d->q_dtype != SKV_F32 && d->q_dtype != SKV_BF16 && d->q_dtype != SKV_F16) return SKV_ERR_DTYPE;
   if (d->kv_dtype < SKV_F32 || d->kv_dtype > SKV_FP8_E4M3) return SKV_ERR_DTYPE;
   if (d->v_layout != SKV_V_PLAIN && d->v_layout != SKV_V_TRANSPOSED) return SKV_ERR_SHAPE;
   if (d->has_sink != 0 && d->has_sink != 1) return SKV_ERR_SHAPE;

@@ -1,4 +1,5 @@
-// Matrix-core partial kernel for BF16 queries over BF16, INT8 or FP8 KV.
+// Matrix-core partial kernel for BF16 queries over BF16, INT8 or FP8 KV and
+// FP16 queries over INT8 or FP8 KV.
 //
 // What it computes is one split of the split-KV method (tiny-llm #11 split-KV
 // design record, "Design": a partial kernel over (head, split) that derives its
@@ -42,7 +43,9 @@
 //    reproduces every bf16 element within 2^13 of its block maximum exactly;
 //    these products accumulate at about 2^-14 of the sum of their magnitudes
 //    (measured), not at fp32. INT8 and BF16 K convert to bf16 (exactly) for
-//    v_mfma_f32_32x32x16_bf16. V codes always convert to bf16 exactly. The
+//    v_mfma_f32_32x32x16_bf16. With an fp16 query, INT8 and FP8 K convert to
+//    fp16 (exactly) for v_mfma_f32_32x32x16_f16, the query keeping all its
+//    bits. V codes always convert to bf16 exactly. The
 //    per-token K scale multiplies the logits and the per-token V scale the
 //    probabilities, so the other rounding is P -> bf16.
 //  * The softmax is online with lazy rescaling: the running maximum of a row
@@ -118,9 +121,33 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t w0, uint32_t w1, uint32_t w2, ui
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 8-bit K codes as fp16 operands for an fp16 query (both conversions exact:
+// e4m3 and int8 values are fp16 values).
+template <class KT>
+__device__ __forceinline__ f16x8 cvt8h(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  if constexpr (__is_same(KT, FP8)) {
+    r = u32x4{fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0), fp8x2_to_f16x2<false>(w1),
+              fp8x2_to_f16x2<true>(w1)};
+  } else {
+    static_assert(__is_same(KT, I8), "fp16 queries take 8-bit K codes");
+    r = u32x4{pack_f16x2(i8_to_f32(w0, 0), i8_to_f32(w0, 1)), pack_f16x2(i8_to_f32(w0, 2), i8_to_f32(w0, 3)),
+              pack_f16x2(i8_to_f32(w1, 0), i8_to_f32(w1, 1)), pack_f16x2(i8_to_f32(w1, 2), i8_to_f32(w1, 3))};
+  }
+  return __builtin_bit_cast(f16x8, r);
+}
+
 __device__ __forceinline__ floatx16 mfma(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ floatx16 mfma(f16x8 a, f16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Query operand type of S^T = K Q^T: the query's own 16-bit format.
+template <class QT> struct QOperand { typedef bf16x8 type; };
+template <> struct QOperand<F16> { typedef f16x8 type; };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -170,7 +197,7 @@ __device__ __forceinline__ int cload(const int* p) {
   return *(const __attribute__((address_space(4))) int*)p;
 }
 
-template <class KT, int D, int NRH, bool VT>
+template <class QT, class KT, int D, int NRH, bool VT>
 __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int EB = Storage<KT>::bytes;
   constexpr bool QUANT = Storage<KT>::quant;
@@ -191,10 +218,13 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int U = DB * EB;                     // transposed V: 512-byte units per group
   static_assert(RB >= 64 && RB % 64 == 0, "key rows of 64, 128 or 256 bytes");
   constexpr int QS = D + 8;                      // LDS row stride of Q (bf16), padded
-  // FP8 K: S^T = K Q^T runs on the fp8 matrix cores (32x32x64 with block
-  // scales), Q split once per workgroup into an fp8 high part and an fp8
-  // residual; other codes convert K to bf16.
-  constexpr bool F8QK = __is_same(KT, FP8);
+  // FP8 K with a bf16 query: S^T = K Q^T runs on the fp8 matrix cores
+  // (32x32x64 with block scales), Q split once per workgroup into an fp8 high
+  // part and an fp8 residual; otherwise K is converted to the query's 16-bit
+  // format (bf16 or fp16) and multiplied on the 16-bit matrix cores. P V is
+  // always a bf16 product.
+  constexpr bool F8QK = __is_same(KT, FP8) && __is_same(QT, BF16);
+  typedef typename QOperand<QT>::type qop;
   constexpr int QS8 = D + 16;                    // LDS row stride of the fp8 Q parts, padded
   constexpr int QBYTES = F8QK ? 2 * ROWS * QS8 + ROWS * (D / 32) * 2 : ROWS * QS * 2;
   constexpr int BUDGET = 156 * 1024;
@@ -426,12 +456,12 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   u32x4 qa[KS8][2], qb[KS8][2];
   constexpr int KPC = 16 / (8 * EB);              // k-steps per 16-byte chunk
   constexpr int KS = NCH * KPC;                   // k-steps of 16 d
-  bf16x8 qf[F8QK ? 1 : KS];
+  qop qf[F8QK ? 1 : KS];
   // Stage the group's query rows in LDS and read this lane's operand parts
   // back (called once the first blocks' loads are in flight, so their
   // latency overlaps the query loads).
   auto stage_q = [&]() __attribute__((always_inline)) {
-    // Query rows of the group -> LDS (bf16, rows padded by 16 bytes); rows past
+    // Query rows of the group -> LDS (bf16 or fp16 as given, rows padded by 16 bytes); rows past
     // rho are zero. The B operand of S^T = K Q^T is read back per k-step:
     // lane holds row i32 of the wave's rows, d in [hh * D/2 + 8 kk, +8).
     if constexpr (F8QK) {
@@ -509,7 +539,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     if constexpr (!F8QK) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
+        qf[kk] = __builtin_bit_cast(qop, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
     }
     if constexpr (F8QK) {                          // (the split Q rows are in LDS: barrier above)
 #pragma unroll
@@ -569,8 +599,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 #pragma unroll
       for (int h2 = 0; h2 < KPC; ++h2) {
         const int kk = c * KPC + h2;
-        bf16x8 kf;
-        if constexpr (EB == 1) {
+        qop kf;
+        if constexpr (__is_same(QT, F16)) {
+          kf = cvt8h<KT>(kc[c][2 * h2], kc[c][2 * h2 + 1]);
+        } else if constexpr (EB == 1) {
           kf = cvt8<KT>(kc[c][2 * h2], kc[c][2 * h2 + 1], 0u, 0u);
         } else {
           kf = cvt8<KT>(kc[c][0], kc[c][1], kc[c][2], kc[c][3]);
@@ -904,24 +936,24 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 
 namespace {
 
-template <class KT, int D, int NRH>
+template <class QT, class KT, int D, int NRH>
 int launch_v(const Params& p, void* stream, int64_t grid) {
   if (p.v_layout == SKV_V_TRANSPOSED)
-    hipLaunchKernelGGL((partial_mfma<KT, D, NRH, true>), dim3((unsigned)grid), dim3(256 * NRH), 0,
+    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, true>), dim3((unsigned)grid), dim3(256 * NRH), 0,
                        (hipStream_t)stream, p);
   else
-    hipLaunchKernelGGL((partial_mfma<KT, D, NRH, false>), dim3((unsigned)grid), dim3(256 * NRH), 0,
+    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, false>), dim3((unsigned)grid), dim3(256 * NRH), 0,
                        (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ERR_LAUNCH;
 }
 
-template <class KT>
+template <class QT, class KT>
 int launch_d(const Params& p, int nrh, void* stream, int64_t grid) {
   switch (p.D) {
-    case 64: return nrh == 2 ? launch_v<KT, 64, 2>(p, stream, grid) : launch_v<KT, 64, 1>(p, stream, grid);
-    case 128: return nrh == 2 ? launch_v<KT, 128, 2>(p, stream, grid) : launch_v<KT, 128, 1>(p, stream, grid);
+    case 64: return nrh == 2 ? launch_v<QT, KT, 64, 2>(p, stream, grid) : launch_v<QT, KT, 64, 1>(p, stream, grid);
+    case 128: return nrh == 2 ? launch_v<QT, KT, 128, 2>(p, stream, grid) : launch_v<QT, KT, 128, 1>(p, stream, grid);
     case 256:
-      if constexpr (Storage<KT>::bytes == 1) return launch_v<KT, 256, 1>(p, stream, grid);
+      if constexpr (Storage<KT>::bytes == 1) return launch_v<QT, KT, 256, 1>(p, stream, grid);
       return SKV_ERR_UNSUPPORTED;
   }
   return SKV_ERR_SHAPE;
@@ -930,8 +962,15 @@ int launch_d(const Params& p, int nrh, void* stream, int64_t grid) {
 }  // namespace
 
 bool mfma_supported(const Params& p) {
-  if (p.q_dtype != SKV_BF16) return false;
-  if (p.kv_dtype != SKV_BF16 && p.kv_dtype != SKV_INT8 && p.kv_dtype != SKV_FP8_E4M3) return false;
+  // bf16 queries with bf16 or 8-bit KV; fp16 queries with 8-bit KV (a bf16
+  // key is not an fp16 value: that pair stays on the vector kernel)
+  if (p.q_dtype == SKV_BF16) {
+    if (p.kv_dtype != SKV_BF16 && p.kv_dtype != SKV_INT8 && p.kv_dtype != SKV_FP8_E4M3) return false;
+  } else if (p.q_dtype == SKV_F16) {
+    if (p.kv_dtype != SKV_INT8 && p.kv_dtype != SKV_FP8_E4M3) return false;
+  } else {
+    return false;
+  }
   if (p.D != 64 && p.D != 128 && p.D != 256) return false;
   // a 32-key block of bf16 rows at D = 256 is 32 KiB of K and V: too big for the
   // per-wave LDS ring, so that shape stays on the vector kernel
@@ -948,10 +987,17 @@ int launch_partial_mfma(Params p, void* stream) {
   p.row_groups = (p.rho + rows - 1) / rows;
   const int64_t grid = (int64_t)p.n_items * p.Hkv * p.row_groups;
   if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
+  if (p.q_dtype == SKV_F16) {
+    switch (p.kv_dtype) {
+      case SKV_INT8: return launch_d<F16, I8>(p, nrh, stream, grid);
+      case SKV_FP8_E4M3: return launch_d<F16, FP8>(p, nrh, stream, grid);
+    }
+    return SKV_ERR_DTYPE;
+  }
   switch (p.kv_dtype) {
-    case SKV_BF16: return launch_d<BF16>(p, nrh, stream, grid);
-    case SKV_INT8: return launch_d<I8>(p, nrh, stream, grid);
-    case SKV_FP8_E4M3: return launch_d<FP8>(p, nrh, stream, grid);
+    case SKV_BF16: return launch_d<BF16, BF16>(p, nrh, stream, grid);
+    case SKV_INT8: return launch_d<BF16, I8>(p, nrh, stream, grid);
+    case SKV_FP8_E4M3: return launch_d<BF16, FP8>(p, nrh, stream, grid);
   }
   return SKV_ERR_DTYPE;
 }

@@ -27,6 +27,8 @@ template <class QT>
 __device__ __forceinline__ float load_q(const void* q, int64_t idx) {
   if constexpr (Storage<QT>::bytes == 4) {
     return reinterpret_cast<const float*>(q)[idx];
+  } else if constexpr (__is_same(QT, F16)) {
+    return (float)reinterpret_cast<const _Float16*>(q)[idx];
   } else {
     return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(q)[idx]);
   }
@@ -280,7 +282,9 @@ int launch_partial_valu(Params p, void* stream) {
   p.row_groups = nrc;
   const int64_t grid = (int64_t)p.n_items * p.Hkv * nrc;
   if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
-  return p.q_dtype == SKV_F32 ? launch_kv<F32>(p, stream, grid) : launch_kv<BF16>(p, stream, grid);
+  if (p.q_dtype == SKV_F32) return launch_kv<F32>(p, stream, grid);
+  if (p.q_dtype == SKV_F16) return launch_kv<F16>(p, stream, grid);
+  return launch_kv<BF16>(p, stream, grid);
 }
 
 }  // namespace skv

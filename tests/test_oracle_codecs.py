@@ -1,5 +1,7 @@
 """Pins of the oracle's storage decoders against library routines and known values."""
 
+import math
+
 import numpy as np
 import torch
 
@@ -52,3 +54,26 @@ def test_int8_and_f32_decode():
     assert np.array_equal(oracle.decode_storage(a, "int8"), np.arange(-128, 128, dtype=np.float64))
     f = np.array([1.5, -2.25, 3e-8], dtype=np.float32)
     assert np.array_equal(oracle.decode_storage(f, "f32"), f.astype(np.float64))
+
+
+def test_f16_decode_matches_torch_for_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    ours = oracle.decode_f16_bits(bits)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 * 1023                           # exponent 31 with a nonzero mantissa
+    assert np.array_equal(ours[~nan], lib[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(lib[~nan]))
+
+
+def test_f16_known_values():
+    d = lambda b: float(oracle.decode_storage(np.array([b], dtype=np.uint16), "f16")[0])
+    assert d(0x3C00) == 1.0 and d(0xC000) == -2.0
+    assert d(0x7BFF) == 65504.0                             # largest finite
+    assert d(0x0001) == 2.0 ** -24                          # smallest subnormal
+    assert d(0x03FF) == 1023 * 2.0 ** -24                   # largest subnormal
+    assert d(0x0400) == 2.0 ** -14                          # smallest normal
+    assert d(0x3555) == 1365 / 4096                         # 0.333251953125
+    assert d(0x7C00) == float("inf") and d(0xFC00) == -float("inf")
+    assert math.isnan(d(0x7E00))

@@ -53,6 +53,8 @@ def _torch_decode(codes, kv_dtype):
         return codes.astype(np.float64)
     if kv_dtype == "fp8":
         return torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    if kv_dtype == "f16":
+        return torch.from_numpy(codes.view(np.int16)).view(torch.float16).double().numpy()
     raise ValueError(kv_dtype)
 
 
@@ -64,8 +66,9 @@ def _build_tiny(rng, *, B, R, Hq, Hkv, D, ctx, bs, kv_dtype, q_dtype, v_layout, 
     Ks = (rng.uniform(0.01, 0.05, size=(B, Hkv, Tmax)).astype(np.float32) if quant else None)
     Vs = (rng.uniform(0.01, 0.05, size=(B, Hkv, Tmax)).astype(np.float32) if quant else None)
     qv = rng.standard_normal((B, R, Hq, D)).astype(np.float32)
-    if q_dtype == "bf16":
-        q = torch.from_numpy(qv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if q_dtype in ("bf16", "f16"):
+        qt = torch.bfloat16 if q_dtype == "bf16" else torch.float16
+        q = torch.from_numpy(qv).to(qt).view(torch.int16).numpy().view(np.uint16)
     else:
         q = qv
     sk = rng.standard_normal(Hq).astype(np.float32) if sinks else None
@@ -107,7 +110,7 @@ def _brute_force(logical, *, B, R, Hq, Hkv, D, ctx, causal, window, scale, kv_dt
     if logical["Ks"] is not None:
         K = K * logical["Ks"].astype(np.float64)[..., None]
         V = V * logical["Vs"].astype(np.float64)[..., None]
-    q = _torch_decode(logical["q"], q_dtype) if q_dtype == "bf16" else logical["q"].astype(np.float64)
+    q = _torch_decode(logical["q"], q_dtype) if q_dtype in ("bf16", "f16") else logical["q"].astype(np.float64)
     G = Hq // Hkv
     Tmax = K.shape[2]
     out = np.zeros((B, R, Hq, D))
@@ -141,6 +144,8 @@ CASES = [
     (1, 3, 2, 1, 4, (2,), 16, "fp8", "bf16", True, 0, True, "plain"),      # ctx < R
     (2, 1, 4, 4, 4, (23, 31), 16, "int8", "f32", False, 7, True, "plain"),
     (1, 3, 4, 2, 8, (40,), 3, "bf16", "f32", False, 0, True, "transposed"),  # non-causal MTP
+    (2, 4, 4, 1, 8, (29, 7), 4, "fp8", "f16", True, 0, False, "plain"),      # fp16 queries
+    (1, 2, 4, 2, 8, (25,), 16, "int8", "f16", True, 6, True, "transposed"),
 ]
 
 
