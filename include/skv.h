@@ -85,6 +85,11 @@
  *   m   a reference maximum in log2 units, l = sum_{t in T_s} 2^(x_t log2(e) - m),
  *   acc[D] = sum_{t in T_s} 2^(x_t log2(e) - m) v_t.
  * (m is at least the largest x_t log2(e) - 8, so l and acc stay finite.)
+ * acc is stored as fp32, or as bf16 (round to nearest even) when the
+ * descriptor's record_dtype is SKV_BF16: half the record bytes, the layout of
+ * the planned-reduction page ([PA] Changes: bf16 partial output plus two fp32
+ * per row; here the un-normalised acc with m and l, which carries the same
+ * information).
  * An empty T_s gives m = -inf, l = 0, acc = 0. Record slot numbers:
  *   uniform splits:  slot = ((b * S) + s) * Hkv + g
  *   planned splits:  slot = (req_slot0[b] + s) * Hkv + g
@@ -92,8 +97,8 @@
  * The merge ([DR] Design, Q3; [PA] Changes): M = max over splits with l > 0
  * (and the sink logit in log2 units); L = sum_s 2^(m_s - M) l_s
  * (+ 2^(sink log2(e) - M)); O = (sum_s 2^(m_s - M) acc_s) * (1 / (L + 1e-9)),
- * splits taken in increasing s. With one split this is bit-identical to the
- * single-pass entry points.
+ * splits taken in increasing s. With one split and fp32 records this is
+ * bit-identical to the single-pass entry points.
  */
 #ifndef SKV_H_
 #define SKV_H_
@@ -105,7 +110,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 2
+#define SKV_ABI_VERSION 3
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
 #define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
@@ -152,7 +157,7 @@ typedef struct skv_desc {
   int32_t causal;         /* 1: row j sits at ctx - R + j; 0: every row at ctx - 1 */
   int32_t window;         /* sliding window W in keys, 0 = none */
   float scale;            /* logit scale, usually 1/sqrt(D) */
-  int32_t q_dtype;        /* SKV_F32 or SKV_BF16 (o has the same dtype) */
+  int32_t q_dtype;        /* SKV_F32, SKV_BF16 or SKV_F16 (o has the same dtype) */
   int32_t kv_dtype;       /* skv_dtype */
   int32_t block_size;     /* paged: tokens per page, power of two in [1, 1024] */
   int32_t max_pages;      /* paged: page-table row stride (>= 1) */
@@ -160,6 +165,7 @@ typedef struct skv_desc {
   int32_t v_layout;       /* skv_v_layout */
   int32_t has_sink;       /* 1: args.sinks holds Hq fp32 logits */
   int32_t impl;           /* skv_impl */
+  int32_t record_dtype;   /* partial-record acc: SKV_F32 (0) or SKV_BF16; else SKV_ERR_DTYPE */
 } skv_desc;
 
 /* Device pointers of one call (k_scale / v_scale only for INT8 / FP8 KV,
@@ -177,13 +183,14 @@ typedef struct skv_args {
 } skv_args;
 
 /* Caller-owned partial-record buffers (device memory), sized by
- * skv_workspace_size for `capacity_slots` records. `acc` must be 16-byte
- * aligned (its records are written and read as 4-float vectors);
- * SKV_ERR_ALIGN otherwise. */
+ * skv_workspace_size for `capacity_slots` records. `acc` holds fp32 or bf16
+ * values (the descriptor's record_dtype) and must be 16-byte aligned (its
+ * records are written and read as 4-element vectors); SKV_ERR_ALIGN
+ * otherwise. */
 typedef struct skv_partials {
   float* m;
   float* l;
-  float* acc;
+  void* acc;
   int64_t capacity_slots;
 } skv_partials;
 
@@ -201,8 +208,8 @@ const char* skv_status_str(int status);
 int skv_validate(const skv_desc* d, int32_t paged, int32_t num_splits, const skv_partials* p);
 
 /* Bytes of m, l and acc for `slots` partial records of descriptor d:
- * slots * rho * 4, slots * rho * 4 and slots * rho * D * 4. Any output
- * pointer may be NULL. */
+ * slots * rho * 4, slots * rho * 4 and slots * rho * D * (4, or 2 for bf16
+ * records). Any output pointer may be NULL. */
 int skv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t* l_bytes,
                        size_t* acc_bytes);
 

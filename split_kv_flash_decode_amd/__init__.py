@@ -44,7 +44,7 @@ class Desc(ctypes.Structure):
                 ("window", _c_i32), ("scale", ctypes.c_float), ("q_dtype", _c_i32),
                 ("kv_dtype", _c_i32), ("block_size", _c_i32), ("max_pages", _c_i32),
                 ("kv_capacity", _c_i32), ("v_layout", _c_i32), ("has_sink", _c_i32),
-                ("impl", _c_i32)]
+                ("impl", _c_i32), ("record_dtype", _c_i32)]
 
 
 class Args(ctypes.Structure):
@@ -159,7 +159,7 @@ def _need(cond: bool, msg: str):
 
 def make_desc(q, k, v, *, paged: bool, v_layout: str = "plain", causal: bool = False,
               window: int = 0, scale: Optional[float] = None, page_table=None,
-              has_sink: bool = False, impl: str = "auto") -> Desc:
+              has_sink: bool = False, impl: str = "auto", record_dtype: str = "f32") -> Desc:
     """Build the descriptor of a call from its tensors (shapes, dtypes, layout)."""
     _need(q.dim() == 4 and q.is_contiguous(), "q must be a contiguous [B][R][Hq][D] tensor")
     _need(q.dtype in _Q_CODES, f"q dtype {q.dtype} unsupported")
@@ -179,6 +179,7 @@ def make_desc(q, k, v, *, paged: bool, v_layout: str = "plain", causal: bool = F
     d.v_layout = vl
     d.has_sink = int(bool(has_sink))
     d.impl = {"auto": SKV_IMPL_AUTO, "valu": SKV_IMPL_VALU, "mfma": SKV_IMPL_MFMA}[impl]
+    d.record_dtype = {"f32": SKV_F32, "bf16": SKV_BF16}[record_dtype]
     _need(k.shape[3] == D, "k's last dim must be D")
     if paged:
         _need(page_table is not None and page_table.dtype == torch.int32 and page_table.dim() == 2,
@@ -216,14 +217,18 @@ def make_args(q, k, v, ctx_lens, o, *, k_scale=None, v_scale=None, page_table=No
 
 
 class Workspace:
-    """Caller-owned partial-record buffers (fp32 m, l, acc) for ``slots`` records."""
+    """Caller-owned partial-record buffers for ``slots`` records: fp32 m and l,
+    acc in the descriptor's record dtype (fp32 or bf16)."""
 
     def __init__(self, desc: Desc, slots: int, device, fill: Optional[float] = None):
         mb, lb, ab = workspace_size(desc, slots)
         kw = dict(dtype=torch.float32, device=device)
         self.m = torch.empty(mb // 4, **kw)
         self.l = torch.empty(lb // 4, **kw)
-        self.acc = torch.empty(ab // 4, **kw)
+        if desc.record_dtype == SKV_BF16:
+            self.acc = torch.empty(ab // 2, dtype=torch.bfloat16, device=device)
+        else:
+            self.acc = torch.empty(ab // 4, **kw)
         if fill is not None:
             for t in (self.m, self.l, self.acc):
                 t.fill_(fill)

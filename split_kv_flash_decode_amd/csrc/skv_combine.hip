@@ -10,7 +10,8 @@
 // are 16-byte coalesced and a request with many splits is read by many
 // lanes at once. The quarters are visited in a fixed order, which makes the
 // result deterministic, and with one split bit-identical to the single-pass
-// kernels (same operations as finalize_one).
+// kernels (same operations as finalize_one). bf16 records are widened to
+// fp32 as they are read; the arithmetic is the same.
 
 #include "skv_device.h"
 
@@ -18,6 +19,7 @@ namespace skv {
 
 constexpr int kCombineThreads = 256;
 
+template <bool RBF>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
   const int tpr = p.D >> 2;            // outputs per row
   const int rpw = kCombineThreads / (4 * tpr);   // rows per workgroup
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
   }
   int j, h;
   row_jh(p, g, r, &j, &h);
-  const floatx4 v = merge_splits4(p, g, r, d, h, S, slot0, q);
+  const floatx4 v = merge_splits4<RBF>(p, g, r, d, h, S, slot0, q);
   if (q == 0) store_o4(p, qo_idx(p, b, j, h, d), v);
 }
 
@@ -51,7 +53,10 @@ int launch_combine(Params p, void* stream) {
   const int nch = (p.rho + rpw - 1) / rpw;
   const int64_t grid = (int64_t)p.B * p.Hkv * nch;
   if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, (hipStream_t)stream, p);
+  if (p.rec_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ERR_LAUNCH;
 }
 

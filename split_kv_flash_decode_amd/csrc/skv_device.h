@@ -187,6 +187,22 @@ __device__ __forceinline__ float quad_lane(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xF, 0xF, true));
 }
 
+// Partial-record accumulator stores: fp32, or bf16 by round to nearest even.
+__device__ __forceinline__ void store_rec1(const Params& p, int64_t idx, float x) {
+  if (p.rec_bf16)
+    static_cast<uint16_t*>(p.pacc)[idx] = (uint16_t)(pack_bf16x2(x, 0.0f) & 0xFFFF);
+  else
+    static_cast<float*>(p.pacc)[idx] = x;
+}
+
+__device__ __forceinline__ void store_rec4(const Params& p, int64_t idx, floatx4 x) {
+  if (p.rec_bf16)
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.pacc) + idx) =
+        u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  else
+    *reinterpret_cast<floatx4*>(static_cast<float*>(p.pacc) + idx) = x;
+}
+
 // Running state of a split merge: maximum M, sum L and accumulators a (for
 // four d), all relative to M.
 struct MergeState {
@@ -217,24 +233,34 @@ __device__ __forceinline__ void merge_absorb(MergeState& t, float m, float l, fl
 
 // Records of splits [s_begin, s_end) in increasing order, read in batches of
 // NB whose loads are all in flight together (indices past the range re-read
-// its last split and are skipped).
-template <int NB>
+// its last split and are skipped). RBF: bf16 record accumulators (widened
+// after the whole batch is loaded).
+template <int NB, bool RBF>
 __device__ __forceinline__ MergeState merge_range(const Params& p, int64_t rec0, int64_t rs, int d, int s_begin,
                                                   int s_end) {
   MergeState t{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
   for (int s0 = s_begin; s0 < s_end; s0 += NB) {
     float lb[NB], mb[NB];
     floatx4 ab[NB];
+    u32x2 hb[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s = s0 + i < s_end ? s0 + i : s_end - 1;
       lb[i] = p.pl[rec0 + s * rs];
       mb[i] = p.pm[rec0 + s * rs];
-      ab[i] = *reinterpret_cast<const floatx4*>(p.pacc + (rec0 + s * rs) * p.D + d);
+      const int64_t e = (rec0 + s * rs) * p.D + d;
+      if constexpr (RBF)
+        hb[i] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.pacc) + e);
+      else
+        ab[i] = *reinterpret_cast<const floatx4*>(static_cast<const float*>(p.pacc) + e);
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (RBF)
+        ab[i] = floatx4{__uint_as_float(hb[i][0] << 16), __uint_as_float(hb[i][0] & 0xFFFF0000u),
+                        __uint_as_float(hb[i][1] << 16), __uint_as_float(hb[i][1] & 0xFFFF0000u)};
       if (s0 + i < s_end) merge_absorb(t, mb[i], lb[i], ab[i]);
+    }
   }
   return t;
 }
@@ -249,6 +275,7 @@ __device__ __forceinline__ MergeState merge_range(const Params& p, int64_t rec0,
 // four splits every quarter holds at most one record and the sequence is the
 // per-record one; with one split the operations are those of the single-pass
 // finalize (finalize_one), so S = 1 stays bit-identical to the single pass.
+template <bool RBF>
 __device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, int d, int h, int S, int slot0,
                                                  int q) {
   const int64_t rs = (int64_t)p.Hkv * p.rho;       // record stride between splits
@@ -258,7 +285,8 @@ __device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, 
   // (batch size from the quarter length, the same for every lane of a
   // request: no loads wasted on short quarters; batches of at most eight
   // keep the register count, and so the occupancy, up)
-  const MergeState part = c <= 4 ? merge_range<4>(p, rec0, rs, d, sb, se) : merge_range<8>(p, rec0, rs, d, sb, se);
+  const MergeState part =
+      c <= 4 ? merge_range<4, RBF>(p, rec0, rs, d, sb, se) : merge_range<8, RBF>(p, rec0, rs, d, sb, se);
   MergeState t{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
   merge_absorb(t, quad_lane<0>(part.M), quad_lane<0>(part.L),
                floatx4{quad_lane<0>(part.a[0]), quad_lane<0>(part.a[1]), quad_lane<0>(part.a[2]), quad_lane<0>(part.a[3])});
@@ -331,7 +359,8 @@ __device__ __forceinline__ void fused_merge_tail(const Params& p, int b, int g, 
     const int r = o / tpr, d = 4 * (o - r * tpr);
     int j, h;
     row_jh(p, g, r, &j, &h);
-    const floatx4 v = merge_splits4(p, g, r, d, h, S, slot0, q);
+    const floatx4 v = p.rec_bf16 ? merge_splits4<true>(p, g, r, d, h, S, slot0, q)
+                                 : merge_splits4<false>(p, g, r, d, h, S, slot0, q);
     if (q == 0) store_o4(p, qo_idx(p, b, j, h, d), v);
   }
 }

@@ -46,6 +46,7 @@ int check_desc(const skv_desc* d, int paged) {
   if (d->v_layout != SKV_V_PLAIN && d->v_layout != SKV_V_TRANSPOSED) return SKV_ERR_SHAPE;
   if (d->has_sink != 0 && d->has_sink != 1) return SKV_ERR_SHAPE;
   if (d->impl < SKV_IMPL_AUTO || d->impl > SKV_IMPL_MFMA) return SKV_ERR_UNSUPPORTED;
+  if (d->record_dtype != SKV_F32 && d->record_dtype != SKV_BF16) return SKV_ERR_DTYPE;
   if (paged > 0) {
     if (!is_pow2(d->block_size) || d->block_size > 1024) return SKV_ERR_SHAPE;
     if (d->max_pages < 1) return SKV_ERR_SHAPE;
@@ -121,6 +122,7 @@ skv::Params make_params(const skv_desc* d, const skv_args* a, int paged, int num
   q.v_layout = d->v_layout;
   q.block_size = paged > 0 ? d->block_size : 0;
   q.impl = d->impl;
+  q.rec_bf16 = d->record_dtype == SKV_BF16;
   return q;
 }
 
@@ -271,7 +273,8 @@ int skv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t
   size_t rows = (size_t)slots * (size_t)rho_of(d);
   if (m_bytes) *m_bytes = rows * sizeof(float);
   if (l_bytes) *l_bytes = rows * sizeof(float);
-  if (acc_bytes) *acc_bytes = rows * (size_t)d->head_dim * sizeof(float);
+  if (d->record_dtype != SKV_F32 && d->record_dtype != SKV_BF16) return SKV_ERR_DTYPE;
+  if (acc_bytes) *acc_bytes = rows * (size_t)d->head_dim * (d->record_dtype == SKV_BF16 ? 2 : 4);
   return SKV_OK;
 }
 

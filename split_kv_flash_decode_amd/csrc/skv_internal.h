@@ -22,7 +22,7 @@ struct Params {
   void* o;
   float* pm;
   float* pl;
-  float* pacc;
+  void* pacc;            // fp32 or (rec_bf16) bf16 record accumulators
   const int32_t* plan;   // device plan metadata, or nullptr for uniform splits
   int32_t* counters;     // single-kernel merge: arrival counters [B * Hkv], or nullptr
   int32_t B, R, Hq, Hkv, D, G, rho;
@@ -39,6 +39,7 @@ struct Params {
   int32_t n_items;       // work items in the grid
   int32_t row_groups;    // row groups per (item, KV head)
   int32_t q_dtype, kv_dtype, v_layout, block_size, impl;
+  int32_t rec_bf16;      // 1: record acc in bf16
 };
 
 // Resolved planner hints for the device-side planner.

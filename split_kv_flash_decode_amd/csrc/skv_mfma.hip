@@ -924,7 +924,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     for (int idx = tid; idx < nrow * (D / 4); idx += NT) {
       const int rr = idx / (D / 4), d = 4 * (idx - rr * (D / 4));
       const int64_t rec = slot * p.rho + rbase + rr;
-      *reinterpret_cast<floatx4*>(&p.pacc[rec * D + d]) = merged(rr, d);
+      store_rec4(p, rec * D + d, merged(rr, d));
       if (d == 0) {
         p.pm[rec] = fin_s[rr][0];
         p.pl[rec] = fin_s[rr][1];

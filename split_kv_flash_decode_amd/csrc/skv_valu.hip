@@ -235,7 +235,7 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
         p.pl[rec] = l[rr];
       }
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) p.pacc[rec * D + lane + 64 * k] = acc[rr][k];
+      for (int k = 0; k < DPL; ++k) store_rec1(p, rec * D + lane + 64 * k, acc[rr][k]);
     }
     if (p.counters) fused_merge_tail(p, b, g, 64);
   }

@@ -9,22 +9,22 @@ import torch
 import split_kv_flash_decode_amd as skv
 
 
-def desc_args(p, impl: str = "auto", o: Optional[torch.Tensor] = None):
+def desc_args(p, impl: str = "auto", o: Optional[torch.Tensor] = None, record_dtype: str = "f32"):
     s = p.spec
     o = torch.empty_like(p.q) if o is None else o
     d = skv.make_desc(p.q, p.k, p.v, paged=p.paged, v_layout=s.v_layout, causal=s.causal,
                       window=s.window, scale=s.scale, page_table=p.page_table, has_sink=s.sinks,
-                      impl=impl)
+                      impl=impl, record_dtype=record_dtype)
     a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
                       page_table=p.page_table, sinks=p.sinks)
     return d, a, o
 
 
 def run(p, mode: str = "split", num_splits: int = 1, impl: str = "auto", ws_fill: Optional[float] = None,
-        hints: Optional[dict] = None, sync: bool = True):
+        hints: Optional[dict] = None, sync: bool = True, record_dtype: str = "f32"):
     """mode: "single" (attention_decode[_paged]), "split" (uniform num_splits) or
     "planned" (planner hints ``hints``). Returns (o, workspace or None, plan or None)."""
-    d, a, o = desc_args(p, impl)
+    d, a, o = desc_args(p, impl, record_dtype=record_dtype)
     ws = plan = None
     if mode == "single":
         (skv.attention_decode_paged if p.paged else skv.attention_decode)(d, a)

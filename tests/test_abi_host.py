@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), f"{n} missing from libskv.so"
     assert set(names) == set(skv.EXPORTS), "binding and header disagree"
-    assert skv.abi_version() == 2
+    assert skv.abi_version() == 3
 
 
 def _desc(**kw):
@@ -66,6 +66,10 @@ def test_validation_codes():
     assert skv.validate(bad, True, 0) == -3
     bad = _desc()
     bad.q_dtype = 2
+    assert skv.validate(bad, True, 0) == -3
+    assert skv.validate(_desc(qdt=torch.float16), True, 0) == 0
+    bad = _desc()
+    bad.record_dtype = 3                                   # records are fp32 or bf16
     assert skv.validate(bad, True, 0) == -3
     assert skv.validate(_desc(), True, 257) == -4
     assert skv.validate(_desc(), True, -1) == -4
@@ -116,6 +120,8 @@ def test_workspace_sizes():
     rho = 4 * 8
     assert m == l == 10 * rho * 4
     assert acc == 10 * rho * 256 * 4
+    d16 = _desc(B=3, R=4, Hq=16, Hkv=2, D=256, record_dtype="bf16")
+    assert skv.workspace_size(d16, 10) == (m, l, 10 * rho * 256 * 2)
 
 
 # ---------------------------------------------------------------------------
