@@ -50,8 +50,9 @@
  *    page indices of the pool; an invalid index is undefined behaviour.
  *
  * Shapes and layouts (row-major, innermost last)
- *   q, o          [B][R][Hq][D]   q_dtype (F32 or BF16); o has q's dtype,
- *                                 bf16 results are rounded to nearest even.
+ *   q, o          [B][R][Hq][D]   q_dtype (F32, BF16 or F16); o has q's
+ *                                 dtype, 16-bit results are rounded to
+ *                                 nearest even.
  *   paged k       [pages][Hkv][block_size][D]
  *   paged v       PLAIN: as k;  TRANSPOSED: [pages][Hkv][D][block_size]
  *   paged scales  [pages][Hkv][block_size] fp32 (INT8 / FP8 KV only; one
@@ -63,6 +64,7 @@
  *   ctx_lens      int32 [B] device visible lengths (the keys of a request,
  *                 its R query tokens included)
  *   sinks         fp32 [Hq] per-query-head sink logits (natural-log units)
+ *   tree_mask     uint64 [B][R] verify masks (optional, see below)
  *
  * Semantics (readings of the pages, see the design notes of the repository)
  *   Query head h uses KV head h / (Hq / Hkv). Causal row j of a request of
@@ -71,6 +73,18 @@
  *   t > p_j - W. The logit of key t is x_t = scale * k_scale_t * <q, code_t>.
  *   O = sum_t e^(x_t - M) v_t / (sum_t e^(x_t - M) [+ e^(sink_h - M)]).
  *   A row that sees no key outputs 0 (with or without a sink).
+ *
+ * Verify masks ([VS] Summary names tree-structured and independent-batch
+ * verification beside the causal multi-row route without defining them; the
+ * reading here): the R query tokens of a causal request are the draft tokens
+ * at keys ctx - R .. ctx - 1, in an order where every token comes after its
+ * ancestors. With args.tree_mask set, row j sees the committed prefix
+ * t < ctx - R as before, and draft key ctx - R + i only when bit i of
+ * tree_mask[b * R + j] is set (and i <= j: a row never sees a later draft).
+ * Causal verification is the mask with bits 0..j set; tree verification sets
+ * the bits of the token's ancestors and itself; independent-batch
+ * verification sets bit j alone. Requires causal = 1, window = 0 and R <= 64
+ * (SKV_ERR_UNSUPPORTED otherwise). Split ranges and records are unchanged.
  *
  * Split ranges ([DR] Design; [PA] Changes). For a request with S splits the
  * split range is [u, ctx) where u = 0, or with a window the earliest row's
@@ -169,7 +183,8 @@ typedef struct skv_desc {
 } skv_desc;
 
 /* Device pointers of one call (k_scale / v_scale only for INT8 / FP8 KV,
- * page_table only for paged calls, sinks only with has_sink). */
+ * page_table only for paged calls, sinks only with has_sink, tree_mask
+ * optional). */
 typedef struct skv_args {
   const void* q;
   const void* k;
@@ -180,6 +195,7 @@ typedef struct skv_args {
   const int32_t* ctx_lens;
   const float* sinks;
   void* o;
+  const uint64_t* tree_mask;   /* NULL, or [B][R] verify masks (see above) */
 } skv_args;
 
 /* Caller-owned partial-record buffers (device memory), sized by

@@ -31,7 +31,12 @@ Readings taken where the pages are silent (each is listed in the design doc):
   value vector, taken in natural-log units and not multiplied by the scale;
 * a row that sees no key outputs 0, with or without a sink;
 * split boundaries are aligned to ``SPLIT_ALIGN`` tokens and cover only the
-  union of the rows' visible ranges (window start aligned down).
+  union of the rows' visible ranges (window start aligned down);
+* verify masks (hipfire #760, Summary, names tree-structured and
+  independent-batch verification without defining them): the R query tokens
+  are drafts at keys ctx - R .. ctx - 1, ancestors before descendants; row j
+  sees the prefix t < ctx - R and draft key ctx - R + i only when bit i of its
+  mask word is set, and never a key after its own position.
 
 The plain attention below uses exact division (no 1e-9 term: its relative
 effect is below 1e-9 whenever the denominator is at least 1, which holds since
@@ -62,6 +67,14 @@ def visible_range(ctx: int, R: int, j: int, causal: bool, window: int) -> Tuple[
     hi = min(p + 1, ctx)
     lo = 0 if window <= 0 else max(0, p - window + 1)
     return max(lo, 0), max(hi, 0)
+
+
+def verify_keys(ctx: int, R: int, j: int, mask_word: int, lo: int, hi: int) -> np.ndarray:
+    """Keys of [lo, hi) that causal row j sees under its verify mask word:
+    every prefix key t < ctx - R, and draft key ctx - R + i when bit i is set."""
+    base = ctx - R
+    keys = [t for t in range(lo, hi) if t < base or (mask_word >> (t - base)) & 1]
+    return np.array(keys, dtype=np.int64)
 
 
 def _dequant(codes, scales, dtype):
@@ -114,7 +127,9 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
     """O[b][j][h][:] = softmax over visible t of scale * <q, k_t> (with sink) applied to V.
 
     Two-pass softmax in float64 over the gathered, dequantized cache. Returns a
-    float64 array [len(requests)][R][Hq][D] (all requests by default).
+    float64 array [len(requests)][R][Hq][D] (all requests by default). With
+    ``arrays["tree_mask"]`` (int64 [B][R] bit patterns) the visible keys of a
+    causal row are further restricted by its verify mask (``verify_keys``).
     """
     q = decode_storage(arrays["q"], q_dtype)
     ctx = np.asarray(arrays["ctx"], dtype=np.int64)
@@ -122,6 +137,7 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
     if has_sink:
         sinks = np.asarray(arrays["sinks"], dtype=np.float32).astype(np.float64)
     G = Hq // Hkv
+    tree = arrays.get("tree_mask")
     reqs = list(range(q.shape[0])) if requests is None else list(requests)
     out = np.zeros((len(reqs), R, Hq, D), dtype=np.float64)
     for i, b in enumerate(reqs):
@@ -132,11 +148,14 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
                               block_size=block_size, v_layout=v_layout)
         for j in range(R):
             lo, hi = visible_range(n, R, j, causal, window)
-            if hi <= lo:
+            keys = np.arange(lo, hi)
+            if tree is not None:
+                keys = verify_keys(n, R, j, int(tree[b, j]) & ((1 << 64) - 1), lo, hi)
+            if keys.size == 0:
                 continue                                   # no visible key: O = 0
             for g in range(Hkv):
                 heads = slice(g * G, (g + 1) * G)
-                x = scale * (q[b, j, heads] @ K[g, lo:hi].T)     # [G][n_vis]
+                x = scale * (q[b, j, heads] @ K[g, keys].T)      # [G][n_vis]
                 M = x.max(axis=1)
                 if sinks is not None:
                     M = np.maximum(M, sinks[heads])
@@ -144,7 +163,7 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
                 L = e.sum(axis=1)
                 if sinks is not None:
                     L = L + np.exp(sinks[heads] - M)
-                out[i, j, heads] = (e @ V[g, lo:hi]) / L[:, None]
+                out[i, j, heads] = (e @ V[g, keys]) / L[:, None]
     return out
 
 

@@ -49,6 +49,7 @@ class ProblemSpec:
     partitions_per_request: int = 0            # explicit planner budget (0 = automatic)
     pool_factor: float = 1.25
     poison: bool = True
+    verify: str = "causal"         # "causal" (no mask) | "chain" | "tree" | "independent" masks
 
     @property
     def G(self) -> int:

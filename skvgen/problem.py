@@ -18,6 +18,11 @@ device the problem is built on, in this order):
 6. A random permutation of the P pool pages; request b takes the next
    ceil(ctx_b / bs) of them as its logical pages 0, 1, ...  P is
    max(N + 1, ceil(1.25 N)) for N referenced pages, so spare pages exist.
+7. Verify masks (``spec.verify`` other than "causal"), int64 [B][R]: "chain"
+   sets bits 0..j of row j; "independent" bit j alone; "tree" draws, per
+   request, a parent for each draft i (uniform over the prefix root and the
+   drafts 0..i-1, one torch.randint per draft) and sets the bits of i and its
+   ancestors.
 
 Poison (``spec.poison``): every spare pool page, and every slot of a request's
 last page at or beyond its context length, is filled with NaN (fp32/bf16),
@@ -58,6 +63,7 @@ class Problem:
     ctx: torch.Tensor                  # int32 [B]
     sinks: Optional[torch.Tensor]      # fp32 [Hq]
     kv_capacity: int                   # contiguous tokens per (request, KV head)
+    tree_mask: Optional[torch.Tensor] = None   # int64 [B][R] verify masks
 
     @property
     def device(self) -> torch.device:
@@ -73,7 +79,7 @@ class Problem:
         return dataclasses.replace(
             self, q=mv(self.q), k=mv(self.k), v=mv(self.v), k_scale=mv(self.k_scale),
             v_scale=mv(self.v_scale), page_table=mv(self.page_table), ctx=mv(self.ctx),
-            sinks=mv(self.sinks))
+            sinks=mv(self.sinks), tree_mask=mv(self.tree_mask))
 
     def host_arrays(self) -> dict:
         """Storage as numpy arrays: bf16 and fp16 as uint16 bit patterns, fp8 as uint8 codes."""
@@ -85,7 +91,8 @@ class Problem:
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
         return {name: np_store(getattr(self, name))
-                for name in ("q", "k", "v", "k_scale", "v_scale", "page_table", "ctx", "sinks")}
+                for name in ("q", "k", "v", "k_scale", "v_scale", "page_table", "ctx", "sinks",
+                             "tree_mask")}
 
 
 def _encode_rows(x: torch.Tensor, kv_dtype: str):
@@ -188,8 +195,33 @@ def make_problem(spec: ProblemSpec, seed: int, device="cpu", paged: bool = True,
         v = v.transpose(-1, -2).contiguous()
 
     ctx = torch.tensor(spec.ctx, dtype=torch.int32, device=dev)
+    tree = verify_masks(spec, g) if spec.verify != "causal" else None
     return Problem(spec=spec, paged=True, q=q, k=k, v=v, k_scale=ks, v_scale=vs,
-                   page_table=table, ctx=ctx, sinks=sinks, kv_capacity=max_pages * bs)
+                   page_table=table, ctx=ctx, sinks=sinks, kv_capacity=max_pages * bs,
+                   tree_mask=None if tree is None else tree.to(dev))
+
+
+def verify_masks(spec: ProblemSpec, g: torch.Generator) -> torch.Tensor:
+    """int64 [B][R] verify masks of ``spec.verify`` (recipe step 7); bit i of
+    row j: draft i is visible to row j."""
+    B, R = spec.B, spec.R
+    assert R <= 64
+    rows = []
+    for _ in range(B):
+        m = []
+        for i in range(R):
+            if spec.verify == "chain":
+                w = (1 << (i + 1)) - 1
+            elif spec.verify == "independent":
+                w = 1 << i
+            elif spec.verify == "tree":
+                par = int(torch.randint(-1, i, (1,), generator=g, device=g.device)) if i > 0 else -1
+                w = (m[par] if par >= 0 else 0) | (1 << i)
+            else:
+                raise ValueError(spec.verify)
+            m.append(w)
+        rows.append([w - (1 << 64) if w >= 1 << 63 else w for w in m])   # as int64 bits
+    return torch.tensor(rows, dtype=torch.int64)
 
 
 def to_contiguous(p: Problem, capacity: Optional[int] = None) -> Problem:
@@ -253,4 +285,5 @@ def extract_request(p: Problem, b: int) -> Problem:
         page_table=torch.arange(n, dtype=torch.int32).view(1, n),
         ctx=torch.tensor([c], dtype=torch.int32),
         sinks=None if p.sinks is None else p.sinks.cpu(),
-        kv_capacity=n * spec.block_size)
+        kv_capacity=n * spec.block_size,
+        tree_mask=None if p.tree_mask is None else p.tree_mask[b:b + 1].cpu())

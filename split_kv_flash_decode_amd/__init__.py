@@ -50,7 +50,7 @@ class Desc(ctypes.Structure):
 class Args(ctypes.Structure):
     _fields_ = [("q", _c_ptr), ("k", _c_ptr), ("v", _c_ptr), ("k_scale", _c_ptr),
                 ("v_scale", _c_ptr), ("page_table", _c_ptr), ("ctx_lens", _c_ptr),
-                ("sinks", _c_ptr), ("o", _c_ptr)]
+                ("sinks", _c_ptr), ("o", _c_ptr), ("tree_mask", _c_ptr)]
 
 
 class Partials(ctypes.Structure):
@@ -196,10 +196,11 @@ def make_desc(q, k, v, *, paged: bool, v_layout: str = "plain", causal: bool = F
 
 
 def make_args(q, k, v, ctx_lens, o, *, k_scale=None, v_scale=None, page_table=None,
-              sinks=None) -> Args:
+              sinks=None, tree_mask=None) -> Args:
     dev = q.device
     for name, t in (("k", k), ("v", v), ("ctx_lens", ctx_lens), ("o", o), ("k_scale", k_scale),
-                    ("v_scale", v_scale), ("page_table", page_table), ("sinks", sinks)):
+                    ("v_scale", v_scale), ("page_table", page_table), ("sinks", sinks),
+                    ("tree_mask", tree_mask)):
         if t is not None:
             _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
             _need(t.is_contiguous(), f"{name} must be contiguous")
@@ -213,6 +214,10 @@ def make_args(q, k, v, ctx_lens, o, *, k_scale=None, v_scale=None, page_table=No
     a.q, a.k, a.v, a.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
     a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
     a.page_table, a.ctx_lens, a.sinks = _ptr(page_table), _ptr(ctx_lens), _ptr(sinks)
+    if tree_mask is not None:
+        _need(tree_mask.dtype in (torch.int64, torch.uint64) and tuple(tree_mask.shape) == tuple(q.shape[:2]),
+              "tree_mask must be a 64-bit integer [B][R] tensor")
+        a.tree_mask = _ptr(tree_mask)
     return a
 
 

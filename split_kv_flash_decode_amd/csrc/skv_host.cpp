@@ -64,6 +64,7 @@ int check_args(const skv_desc* d, const skv_args* a, int paged) {
   bool quant = d->kv_dtype == SKV_INT8 || d->kv_dtype == SKV_FP8_E4M3;
   if (quant && (!a->k_scale || !a->v_scale)) return SKV_ERR_NULL;
   if (d->has_sink && !a->sinks) return SKV_ERR_NULL;
+  if (a->tree_mask && (d->causal != 1 || d->window != 0 || d->q_rows > 64)) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 
@@ -88,6 +89,7 @@ skv::Params make_params(const skv_desc* d, const skv_args* a, int paged, int num
   q.ctx = a->ctx_lens;
   q.sinks = d->has_sink ? a->sinks : nullptr;
   q.o = a->o;
+  q.tree_mask = a->tree_mask;
   if (p) {
     q.pm = p->m;
     q.pl = p->l;

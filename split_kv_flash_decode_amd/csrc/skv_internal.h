@@ -20,6 +20,7 @@ struct Params {
   const int32_t* ctx;
   const float* sinks;
   void* o;
+  const uint64_t* tree_mask;  // verify masks [B][R], or nullptr
   float* pm;
   float* pl;
   void* pacc;            // fp32 or (rec_bf16) bf16 record accumulators
@@ -101,6 +102,13 @@ SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, in
 }
 
 // Visible key range [vlo, vhi) of query row j.
+// Bit of a verify mask for key t of a row (draft keys start at dbase =
+// ctx - R; the prefix is always visible). The shift count is wrapped so that
+// keys past ctx, which other tests mask, stay defined.
+SKV_HD bool tree_visible(uint64_t mask, int t, int dbase) {
+  return t < dbase || ((mask >> ((unsigned)(t - dbase) & 63u)) & 1ull) != 0;
+}
+
 SKV_HD void row_range(int ctx, int R, int causal, int window, int j, int* vlo, int* vhi) {
   int p = causal ? ctx - R + j : ctx - 1;
   int hi = p + 1;

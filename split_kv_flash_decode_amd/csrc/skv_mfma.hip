@@ -197,7 +197,7 @@ __device__ __forceinline__ int cload(const int* p) {
   return *(const __attribute__((address_space(4))) int*)p;
 }
 
-template <class QT, class KT, int D, int NRH, bool VT>
+template <class QT, class KT, int D, int NRH, bool VT, bool TM>
 __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int EB = Storage<KT>::bytes;
   constexpr bool QUANT = Storage<KT>::quant;
@@ -291,7 +291,13 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
   const int wrow0 = rbase + 32 * rh;
   int vlo = 0, vhi = 0;
-  if (wrow0 + i32 < p.rho) row_range(ctx, p.R, p.causal, p.window, (wrow0 + i32) / p.G, &vlo, &vhi);
+  uint64_t tmask = ~0ull;                        // TM: this lane's row's verify mask
+  if (wrow0 + i32 < p.rho) {
+    row_range(ctx, p.R, p.causal, p.window, (wrow0 + i32) / p.G, &vlo, &vhi);
+    if constexpr (TM) tmask = p.tree_mask[(int64_t)b * p.R + (wrow0 + i32) / p.G];
+  }
+  // with verify masks, blocks reaching the draft keys take the masked path
+  const int dbase = TM ? ctx - p.R : 0x7FFFFFFF;
   // Keys every row of the wave sees: [ilo, ihi) (empty for a wave past rho).
   int ilo = 0, ihi = 0;
   if (wrow0 < p.rho) {
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   auto compute = [&](int t0, int st, auto&& mid) __attribute__((always_inline)) {
     const char* S = ring + st * STAGE;
     const bool boundary =
-        __builtin_amdgcn_readfirstlane((int)((t0 + 32 > hi) | (t0 < ilo) | (t0 + 32 > ihi))) != 0;
+        __builtin_amdgcn_readfirstlane((int)((t0 + 32 > hi) | (t0 < ilo) | (t0 + 32 > ihi) | (TM && t0 + 32 > dbase))) != 0;
     const int kb = 16 * hh;                       // first key of this lane's 16
     // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
     floatx16 s;
@@ -695,7 +701,8 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int k = t0 + kb + v;
-        const bool vis = (k < hi) & (k >= vlo) & (k < vhi);
+        bool vis = (k < hi) & (k >= vlo) & (k < vhi);
+        if constexpr (TM) vis &= tree_visible(tmask, k, dbase);
         s[v] = vis ? s[v] : -INFINITY;
       }
     }
@@ -936,14 +943,24 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 
 namespace {
 
+template <class QT, class KT, int D, int NRH, bool VT>
+void launch_tm(const Params& p, void* stream, int64_t grid) {
+  // verify masks get their own instantiation: the plain kernels keep no mask
+  // registers and no extra boundary test
+  if (p.tree_mask)
+    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, VT, true>), dim3((unsigned)grid), dim3(256 * NRH), 0,
+                       (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, VT, false>), dim3((unsigned)grid), dim3(256 * NRH), 0,
+                       (hipStream_t)stream, p);
+}
+
 template <class QT, class KT, int D, int NRH>
 int launch_v(const Params& p, void* stream, int64_t grid) {
   if (p.v_layout == SKV_V_TRANSPOSED)
-    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, true>), dim3((unsigned)grid), dim3(256 * NRH), 0,
-                       (hipStream_t)stream, p);
+    launch_tm<QT, KT, D, NRH, true>(p, stream, grid);
   else
-    hipLaunchKernelGGL((partial_mfma<QT, KT, D, NRH, false>), dim3((unsigned)grid), dim3(256 * NRH), 0,
-                       (hipStream_t)stream, p);
+    launch_tm<QT, KT, D, NRH, false>(p, stream, grid);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ERR_LAUNCH;
 }
 

@@ -16,7 +16,7 @@ def desc_args(p, impl: str = "auto", o: Optional[torch.Tensor] = None, record_dt
                       window=s.window, scale=s.scale, page_table=p.page_table, has_sink=s.sinks,
                       impl=impl, record_dtype=record_dtype)
     a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
-                      page_table=p.page_table, sinks=p.sinks)
+                      page_table=p.page_table, sinks=p.sinks, tree_mask=p.tree_mask)
     return d, a, o
 
 

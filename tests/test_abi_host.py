@@ -114,6 +114,20 @@ def test_compute_calls_fail_closed_without_launching():
         assert isinstance(skv.status_str(s), str) and skv.status_str(s)
 
 
+def test_verify_masks_need_causal_rows_without_window():
+    L = skv.lib()
+    fake = 1 << 20                                        # never dereferenced: the call fails first
+    for kw, setup in ((dict(), lambda d: setattr(d, "window", 8)),
+                      (dict(), lambda d: setattr(d, "causal", 0)),
+                      (dict(R=65), lambda d: None)):
+        d = _desc(**kw)
+        setup(d)
+        a = skv.Args(fake, fake, fake, fake, fake, fake, fake, None, fake, fake)
+        assert L.skv_attention_decode_paged(ctypes.byref(d), ctypes.byref(a), None) == -6
+        a.tree_mask = None
+        assert L.skv_validate(ctypes.byref(d), 1, 0, None) == 0
+
+
 def test_workspace_sizes():
     d = _desc(B=3, R=4, Hq=16, Hkv=2, D=256)
     m, l, acc = skv.workspace_size(d, 10)

@@ -212,6 +212,87 @@ def test_identical_keys_give_mean_of_visible_values(ctx, R, causal, window, v_la
         np.testing.assert_allclose(out[0, j, :, 1], 1.0, rtol=0, atol=1e-14)
 
 
+def _as_int64_bits(words):
+    return np.array([[w - (1 << 64) if w >= 1 << 63 else w for w in row] for row in words], dtype=np.int64)
+
+
+@pytest.mark.parametrize("ctx,R,kind", [
+    (23, 4, "independent"), (23, 4, "tree"), (64, 16, "tree"), (64, 16, "independent"),
+    (3, 4, "tree"), (4, 4, "independent"), (70, 64, "tree"), (70, 64, "high_bits"),
+])
+def test_identical_keys_under_verify_masks_give_mean_of_visible_values(ctx, R, kind):
+    """Equal logits: each row averages exactly the keys its mask lets through,
+    so the position-coded column pins the visible set (prefix keys below
+    ctx - R, the masked drafts, none after the row's own position)."""
+    rng = np.random.default_rng(ctx + R)
+    words = []
+    for i in range(R):
+        if kind == "independent":
+            w = 1 << i
+        elif kind == "high_bits":                  # bits after the row: no effect
+            w = ((1 << 64) - 1) ^ ((1 << i) - 1) if i < 64 else 0
+            w &= (1 << 64) - 1
+        else:
+            par = int(rng.integers(-1, i)) if i > 0 else -1
+            w = (words[par] if par >= 0 else 0) | (1 << i)
+        words.append(w)
+    arrays = _const_key_problem(ctx, R)
+    arrays["tree_mask"] = _as_int64_bits([words])
+    out = oracle.decode_attention(arrays, R=R, Hq=2, Hkv=1, D=4, causal=True, window=0,
+                                  scale=0.5, q_dtype="f32", kv_dtype="f32", paged=True,
+                                  block_size=5, v_layout="plain", has_sink=False)
+    base = ctx - R
+    for j in range(R):
+        vis = [t for t in range(0, max(base, 0))]
+        vis += [base + i for i in range(j + 1) if base + i >= 0 and (words[j] >> i) & 1]
+        if not vis:
+            assert np.all(out[0, j] == 0)
+            continue
+        np.testing.assert_allclose(out[0, j, :, 0], float(np.mean(vis)), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out[0, j, :, 1], 1.0, rtol=0, atol=1e-14)
+
+
+def test_chain_mask_equals_causal():
+    rng = np.random.default_rng(77)
+    arrays, _ = _build_tiny(rng, B=2, R=5, Hq=4, Hkv=2, D=8, ctx=(40, 6), bs=4, kv_dtype="fp8",
+                            q_dtype="bf16", v_layout="plain", sinks=True)
+    kw = dict(R=5, Hq=4, Hkv=2, D=8, causal=True, window=0, scale=0.3, q_dtype="bf16", kv_dtype="fp8",
+              paged=True, block_size=4, v_layout="plain", has_sink=True)
+    plain = oracle.decode_attention(arrays, **kw)
+    arrays["tree_mask"] = _as_int64_bits([[(1 << (j + 1)) - 1 for j in range(5)]] * 2)
+    chain = oracle.decode_attention(arrays, **kw)
+    np.testing.assert_array_equal(chain, plain)
+
+
+def test_independent_rows_equal_single_row_problems():
+    """Independent-batch verify: row j equals a one-row, non-causal problem over
+    the prefix and draft j alone (the cache rebuilt without the other drafts)."""
+    rng = np.random.default_rng(78)
+    R, ctx, D = 4, 29, 8
+    arrays, logical = _build_tiny(rng, B=1, R=R, Hq=2, Hkv=1, D=D, ctx=(ctx,), bs=4, kv_dtype="int8",
+                                  q_dtype="f32", v_layout="plain", sinks=False)
+    arrays["tree_mask"] = _as_int64_bits([[1 << j for j in range(R)]])
+    out = oracle.decode_attention(arrays, R=R, Hq=2, Hkv=1, D=D, causal=True, window=0, scale=0.4,
+                                  q_dtype="f32", kv_dtype="int8", paged=True, block_size=4,
+                                  v_layout="plain", has_sink=False)
+    base = ctx - R
+    for j in range(R):
+        keep = list(range(base)) + [base + j]
+        n = len(keep)
+        # pool pages of one token each: [n][Hkv][1][D]
+        k = np.ascontiguousarray(logical["Kc"][0][:, keep].transpose(1, 0, 2)[:, :, None, :])
+        v = np.ascontiguousarray(logical["Vc"][0][:, keep].transpose(1, 0, 2)[:, :, None, :])
+        one = dict(q=logical["q"][:, j:j + 1], k=k, v=v,
+                   k_scale=np.ascontiguousarray(logical["Ks"][0][:, keep].T[:, :, None]),
+                   v_scale=np.ascontiguousarray(logical["Vs"][0][:, keep].T[:, :, None]),
+                   page_table=np.arange(n, dtype=np.int32).reshape(1, n),
+                   ctx=np.array([n], dtype=np.int32), sinks=None)
+        ref = oracle.decode_attention(one, R=1, Hq=2, Hkv=1, D=D, causal=False, window=0, scale=0.4,
+                                      q_dtype="f32", kv_dtype="int8", paged=True, block_size=1,
+                                      v_layout="plain", has_sink=False)
+        np.testing.assert_allclose(out[0, j], ref[0, 0], rtol=0, atol=1e-13)
+
+
 @pytest.mark.parametrize("sink", [-3.0, 0.0, 0.7, 5.0])
 def test_identical_keys_with_sink_closed_form(sink):
     ctx, R = 19, 2
