@@ -158,7 +158,9 @@ typedef enum skv_dtype {
 typedef enum skv_v_layout { SKV_V_PLAIN = 0, SKV_V_TRANSPOSED = 1 } skv_v_layout;
 
 /* Kernel family selection. AUTO picks the matrix-core kernel when q is BF16
- * and KV is BF16, INT8 or FP8, else the vector kernel. */
+ * and KV is BF16, INT8 or FP8, or q is F16 and KV is INT8 or FP8 (page size
+ * >= 16; not BF16 KV at D 256), else the vector kernel; MFMA outside those
+ * cases is SKV_ERR_UNSUPPORTED. */
 typedef enum skv_impl { SKV_IMPL_AUTO = 0, SKV_IMPL_VALU = 1, SKV_IMPL_MFMA = 2 } skv_impl;
 
 /* Host description of one call; fixed for the life of a captured graph. */
