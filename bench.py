@@ -149,10 +149,16 @@ PAGE_TABLE = [
 ]
 
 
-def timed_steps(spec, seed: int, steps: int, warmup: int):
+def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f32",
+                mode: str = "two_stage"):
     """Generate the workload, run the planned step (host plan refresh, metadata
     copy, partial, combine) ``warmup`` + ``steps`` times; returns
-    (ms per step, partial ms list, combine ms list, plan)."""
+    (ms per step, partial ms list, combine ms list, plan, problem).
+
+    ``mode`` "fused": the single-kernel split + merge instead of partial +
+    combine (its time is reported as the partial time, combine 0);
+    "device_plan": the plan refreshed on the GPU from the device lengths
+    instead of on the host."""
     import torch
 
     import split_kv_flash_decode_amd as skv
@@ -163,24 +169,34 @@ def timed_steps(spec, seed: int, steps: int, warmup: int):
     torch.cuda.synchronize()
     o = torch.empty_like(p.q)
     d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
-                      window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
+                      window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks,
+                      record_dtype=record_dtype)
     a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
-                      page_table=p.page_table, sinks=p.sinks)
+                      page_table=p.page_table, sinks=p.sinks, tree_mask=p.tree_mask)
     hints = skv.plan_hints(spec.B, spec.R, spec.Hkv, causal=spec.causal, window=spec.window,
                            partitions_per_request=spec.partitions_per_request)
     host_ctx = list(spec.ctx)
     plan = skv.Plan(hints, host_ctx, dev)
     ws = skv.Workspace(d, plan.info.slots, dev)
     stream = torch.cuda.current_stream()
+    counters = torch.zeros(spec.B * spec.Hkv, dtype=torch.int32, device=dev)
 
     def step(ev=None):
-        plan.refresh(host_ctx)
+        if mode == "device_plan":
+            plan.refresh_device(p.ctx)
+        else:
+            plan.refresh(host_ctx)
         if ev is not None:
             ev[0].record(stream)
-        skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
-        if ev is not None:
-            ev[1].record(stream)
-        skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
+        if mode == "fused":
+            skv.splitkv_fused(d, a, True, plan.capacity, ws, counters, plan_meta_dev=plan.dev)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
+            if ev is not None:
+                ev[1].record(stream)
+            skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
         if ev is not None:
             ev[2].record(stream)
 
@@ -221,6 +237,55 @@ def table(args) -> int:
     return 0
 
 
+# The adjacent variants built beside the default path, each timed with the
+# same step on a full-size workload and set against the same workload's
+# default call: (row, config, spec overrides, record dtype, step mode).
+NEXT_ROWS = [
+    ("B200x200k fp8 MTP4 (default call)", 4, {}, "f32", "two_stage"),
+    ("fp16 Q/O", 4, {"q_dtype": "f16"}, "f32", "two_stage"),
+    ("bf16 partial records", 4, {}, "bf16", "two_stage"),
+    ("single-kernel split + merge", 4, {}, "f32", "fused"),
+    ("device-side plan refresh", 4, {}, "f32", "device_plan"),
+    ("MTP4 rows under a random tree mask", 4, {"verify": "tree"}, "f32", "two_stage"),
+    ("int8 verifier R16 (default call)", 3, {}, "f32", "two_stage"),
+    ("int8 verifier, random tree mask", 3, {"verify": "tree"}, "f32", "two_stage"),
+    ("int8 verifier, independent-batch mask", 3, {"verify": "independent"}, "f32", "two_stage"),
+    ("int8 verifier, fp16 Q/O", 3, {"q_dtype": "f16"}, "f32", "two_stage"),
+]
+
+
+def next_rows(args) -> int:
+    import torch
+
+    from skvgen import config_spec
+
+    base = {}
+    for name, n, over, rec, mode in NEXT_ROWS:
+        spec = config_spec(n, **over)
+        small = max(spec.ctx) * spec.B < 10_000_000
+        steps, warmup = (400, 50) if small else (args.steps, args.warmup)
+        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, record_dtype=rec, mode=mode)
+        part_us = sum(part_ms) / len(part_ms) * 1e3
+        unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
+        alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
+        row = {"row": name, "workload": workload_name(spec), "us_per_step": round(ms * 1e3, 2),
+               "effective_TBps": round(spec_bytes(spec) / (ms * 1e-3) / 1e12, 3),
+               "partial_us_mean": round(part_us, 2),
+               "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+               "partial_roofline_frac": round(alg / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+               "steps": steps, "warmup": warmup}
+        if mode == "fused":
+            row["note"] = "partial_us_mean is the fused kernel (split + merge)"
+        if n not in base:
+            base[n] = ms
+        else:
+            row["time_vs_default_call"] = round(ms / base[n], 4)
+        print(json.dumps(row), flush=True)
+        del p
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +302,9 @@ def main(argv=None) -> int:
     ap.add_argument("--table", action="store_true",
                     help="time the six rows of the planned-reduction page's Performance table "
                          "(one JSON line per row, with the page's own time beside ours)")
+    ap.add_argument("--next", action="store_true",
+                    help="time the adjacent variants (fp16 Q/O, bf16 records, fused call, device "
+                         "plan refresh, verify masks) against the default call on the same workloads")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -261,6 +329,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 4 * n, "copies": 3}), flush=True)
         return 0
+    if args.next:
+        return next_rows(args)
     if args.table:
         return table(args)
     overrides = {}
