@@ -173,8 +173,7 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
                       record_dtype=record_dtype)
     a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
                       page_table=p.page_table, sinks=p.sinks, tree_mask=p.tree_mask)
-    hints = skv.plan_hints(spec.B, spec.R, spec.Hkv, causal=spec.causal, window=spec.window,
-                           partitions_per_request=spec.partitions_per_request)
+    hints = skv.plan_hints_for(d, True, partitions_per_request=spec.partitions_per_request)
     host_ctx = list(spec.ctx)
     plan = skv.Plan(hints, host_ctx, dev)
     ws = skv.Workspace(d, plan.info.slots, dev)

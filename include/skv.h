@@ -262,6 +262,12 @@ int skv_attention_decode_paged_splitkv(const skv_desc* d, const skv_args* a, int
  * Items are ordered longest first. A plan's capacity is fixed when it is
  * made; refreshing it with new lengths keeps C (graph replay launches C
  * items) and lowers partition counts if they would exceed it.
+ * Counts: an explicit partitions_per_request takes precedence; otherwise
+ * ceil(span * R / work_per_partition), raised, when the batch does not fill
+ * the base budget num_cus * ctas_per_cu / (Hkv * workgroups_per_head)
+ * partitions, to the request's span share of it (never below
+ * min_tokens_per_partition keys per partition); always within
+ * [1, min(max_partitions, 64-key tiles of the span)].
  */
 typedef struct skv_plan_hints {
   int32_t batch;                   /* B */
@@ -275,7 +281,7 @@ typedef struct skv_plan_hints {
   int32_t max_partitions;          /* cap on P_b, 0 = SKV_PLAN_DEFAULT_MAX_PARTITIONS */
   int32_t work_per_partition;      /* target key-rows (keys * R) per partition, 0 = 50000 */
   int32_t min_tokens_per_partition;/* 0 = 256 */
-  int32_t reserved;
+  int32_t workgroups_per_head;     /* workgroups one partition of one KV head occupies, 0 = 1 */
   int64_t total_context_length;    /* optional work hint: sum of contexts to size capacity */
 } skv_plan_hints;
 
@@ -289,6 +295,15 @@ typedef struct skv_plan_info {
 
 /* int32 entries of a metadata block for B requests and capacity C. */
 int64_t skv_plan_meta_len(int32_t batch, int32_t capacity_items);
+
+/* Planner hints for calls with descriptor d (paged or contiguous): batch,
+ * rows, heads, causal and window from d, and the budget of the kernel family
+ * d selects. Matrix-core kernel: one workgroup per CU (ctas_per_cu 1) and
+ * one per group of 32 or 64 query rows of a KV head (workgroups_per_head),
+ * so the raise fills at most one round of the GPU. Vector kernel: one-wave
+ * workgroups, 16 per CU, 8 rows each, partitions down to one 64-key tile.
+ * Other fields 0 (defaults); the caller may override any of them. Host-only. */
+int skv_plan_hints_for_desc(const skv_desc* d, int32_t paged, skv_plan_hints* h);
 
 /* Capacity (items) a plan needs for these hints and host context lengths
  * (host_ctx may be NULL when hints->total_context_length sizes it). */

@@ -62,7 +62,7 @@ class PlanHints(ctypes.Structure):
                 ("causal", _c_i32), ("window", _c_i32), ("num_cus", _c_i32),
                 ("ctas_per_cu", _c_i32), ("partitions_per_request", _c_i32),
                 ("max_partitions", _c_i32), ("work_per_partition", _c_i32),
-                ("min_tokens_per_partition", _c_i32), ("reserved", _c_i32),
+                ("min_tokens_per_partition", _c_i32), ("workgroups_per_head", _c_i32),
                 ("total_context_length", ctypes.c_int64)]
 
 
@@ -99,6 +99,7 @@ EXPORTS = {
                                          _c_ptr, ctypes.POINTER(Partials), _c_ptr, _c_ptr]),
     "skv_plan_refresh_device": (ctypes.c_int, [ctypes.POINTER(PlanHints), _c_ptr, _c_i32, _c_ptr,
                                                ctypes.c_int64, _c_ptr]),
+    "skv_plan_hints_for_desc": (ctypes.c_int, [ctypes.POINTER(Desc), _c_i32, ctypes.POINTER(PlanHints)]),
 }
 
 _LIB = None
@@ -336,13 +337,26 @@ def _ctx_array(host_ctx):
 def plan_hints(batch: int, q_rows: int, num_kv_heads: int, *, causal: bool = True, window: int = 0,
                num_cus: int = 0, ctas_per_cu: int = 0, partitions_per_request: int = 0,
                max_partitions: int = 0, work_per_partition: int = 0,
-               min_tokens_per_partition: int = 0, total_context_length: int = 0) -> PlanHints:
+               min_tokens_per_partition: int = 0, workgroups_per_head: int = 0,
+               total_context_length: int = 0) -> PlanHints:
     h = PlanHints()
     h.batch, h.q_rows, h.num_kv_heads = batch, q_rows, num_kv_heads
     h.causal, h.window, h.num_cus, h.ctas_per_cu = int(causal), window, num_cus, ctas_per_cu
     h.partitions_per_request, h.max_partitions = partitions_per_request, max_partitions
     h.work_per_partition, h.min_tokens_per_partition = work_per_partition, min_tokens_per_partition
+    h.workgroups_per_head = workgroups_per_head
     h.total_context_length = total_context_length
+    return h
+
+
+def plan_hints_for(desc: Desc, paged: bool = True, **overrides) -> PlanHints:
+    """skv_plan_hints_for_desc, then any field given in ``overrides``."""
+    h = PlanHints()
+    _check(lib().skv_plan_hints_for_desc(ctypes.byref(desc), int(paged), ctypes.byref(h)),
+           "skv_plan_hints_for_desc")
+    for k, v in overrides.items():
+        _need(hasattr(h, k), f"no planner hint {k}")
+        setattr(h, k, int(v))
     return h
 
 

@@ -147,7 +147,7 @@ int run_partial(skv::Params p, void* stream) {
 // ---- planner ---------------------------------------------------------------
 
 struct Hints {
-  int B, R, Hkv, causal, window, cus, ctas, explicit_p, maxp, work, min_tokens;
+  int B, R, Hkv, causal, window, cus, ctas, wph, explicit_p, maxp, work, min_tokens;
 };
 
 Hints resolve(const skv_plan_hints* h) {
@@ -159,6 +159,7 @@ Hints resolve(const skv_plan_hints* h) {
   r.window = h->window;
   r.cus = h->num_cus > 0 ? h->num_cus : 256;
   r.ctas = h->ctas_per_cu > 0 ? h->ctas_per_cu : 2;
+  r.wph = h->workgroups_per_head > 0 ? h->workgroups_per_head : 1;
   r.explicit_p = h->partitions_per_request;
   r.maxp = h->max_partitions > 0 ? std::min(h->max_partitions, SKV_MAX_SPLITS) : SKV_PLAN_DEFAULT_MAX_PARTITIONS;
   r.work = h->work_per_partition > 0 ? h->work_per_partition : 50000;
@@ -170,7 +171,8 @@ int check_hints(const skv_plan_hints* h) {
   if (!h) return SKV_ERR_NULL;
   if (h->batch < 1 || h->q_rows < 1 || h->num_kv_heads < 1 || h->window < 0) return SKV_ERR_PLAN;
   if (h->partitions_per_request < 0 || h->max_partitions < 0 || h->num_cus < 0 ||
-      h->ctas_per_cu < 0 || h->work_per_partition < 0 || h->min_tokens_per_partition < 0)
+      h->ctas_per_cu < 0 || h->work_per_partition < 0 || h->min_tokens_per_partition < 0 ||
+      h->workgroups_per_head < 0)
     return SKV_ERR_PLAN;
   if (h->batch > (1 << 23)) return SKV_ERR_PLAN;
   return SKV_OK;
@@ -186,9 +188,9 @@ int64_t span_of(const Hints& h, int ctx) {
 // Partition counts from host-known work ([PA] intro and Changes):
 //  * explicit partitions_per_request take precedence (clamped to the tiles);
 //  * otherwise a work floor ceil(span * R / work_per_partition), raised to the
-//    request's share of the base budget num_cus * ctas_per_cu / Hkv items
-//    when the batch would not fill it, but never below min_tokens keys per
-//    partition from that raise;
+//    request's share of the base budget num_cus * ctas_per_cu /
+//    (Hkv * workgroups_per_head) items when the batch would not fill it, but
+//    never below min_tokens keys per partition from that raise;
 //  * every count lies in [1, min(max_partitions, tiles of the span)].
 std::vector<int> partition_counts(const Hints& h, const std::vector<int>& ctx) {
   const int B = (int)ctx.size();
@@ -211,7 +213,7 @@ std::vector<int> partition_counts(const Hints& h, const std::vector<int>& ctx) {
     P[b] = (int)std::max<int64_t>(1, std::min<int64_t>(pb, cap));
   }
   if (h.explicit_p <= 0 && total > 0) {
-    int64_t budget = (int64_t)h.cus * h.ctas / h.Hkv;
+    int64_t budget = (int64_t)h.cus * h.ctas / ((int64_t)h.Hkv * h.wph);
     int64_t sum = 0;
     for (int b = 0; b < B; ++b) sum += P[b];
     if (sum < budget) {
@@ -466,6 +468,35 @@ int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int
   return run_partial(prm, stream);
 }
 
+int skv_plan_hints_for_desc(const skv_desc* d, int32_t paged, skv_plan_hints* h) {
+  int rc = check_desc(d, paged);
+  if (rc) return rc;
+  if (!h) return SKV_ERR_NULL;
+  memset(h, 0, sizeof(*h));
+  h->batch = d->batch;
+  h->q_rows = d->q_rows;
+  h->num_kv_heads = d->num_kv_heads;
+  h->causal = d->causal;
+  h->window = d->window;
+  skv_args none;
+  memset(&none, 0, sizeof(none));
+  const skv::Params prm = make_params(d, &none, paged, 1, nullptr, nullptr, 0);
+  const int rho = (int)rho_of(d);
+  if (use_mfma(prm)) {
+    // one workgroup per CU (its LDS ring), one per row group of a KV head
+    const int rows = skv::mfma_group_rows(d->head_dim, rho);
+    h->ctas_per_cu = 1;
+    h->workgroups_per_head = (rho + rows - 1) / rows;
+  } else {
+    // one-wave workgroups, many per CU; a partition of one 64-key tile
+    // still pays for itself
+    h->ctas_per_cu = 16;
+    h->workgroups_per_head = (rho + skv::kValuRows - 1) / skv::kValuRows;
+    h->min_tokens_per_partition = skv::kSplitAlign;
+  }
+  return SKV_OK;
+}
+
 int skv_plan_refresh_device(const skv_plan_hints* h, const int32_t* ctx_dev, int32_t capacity_items,
                             int32_t* meta_dev, int64_t meta_len, void* stream) {
   int rc = check_hints(h);
@@ -483,6 +514,7 @@ int skv_plan_refresh_device(const skv_plan_hints* h, const int32_t* ctx_dev, int
   d.window = r.window;
   d.cus = r.cus;
   d.ctas = r.ctas;
+  d.wph = r.wph;
   d.explicit_p = r.explicit_p;
   d.maxp = r.maxp;
   d.work = r.work;

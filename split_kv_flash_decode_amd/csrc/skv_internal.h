@@ -45,8 +45,15 @@ struct Params {
 
 // Resolved planner hints for the device-side planner.
 struct PlanDev {
-  int32_t B, R, Hkv, causal, window, cus, ctas, explicit_p, maxp, work, min_tokens, C;
+  int32_t B, R, Hkv, causal, window, cus, ctas, wph, explicit_p, maxp, work, min_tokens, C;
 };
+
+// Query rows one workgroup of the matrix-core partial kernel covers: two row
+// halves of 32 when a KV head has more than 32 rows, one at D 256 (its
+// accumulators need the registers).
+inline int mfma_group_rows(int D, int rho) { return (D == 256 || rho <= 32) ? 32 : 64; }
+// Query rows one wave (workgroup) of the vector partial kernel covers.
+constexpr int kValuRows = 8;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSplitAlign = SKV_SPLIT_ALIGN;

@@ -999,8 +999,8 @@ bool mfma_supported(const Params& p) {
 int launch_partial_mfma(Params p, void* stream) {
   // two row halves (eight waves, two per SIMD) when a KV head has more than
   // 32 query rows; D = 256 keeps one (its accumulators need the registers)
-  const int nrh = (p.D == 256 || p.rho <= 32) ? 1 : 2;
-  const int rows = 32 * nrh;
+  const int rows = mfma_group_rows(p.D, p.rho);
+  const int nrh = rows / 32;
   p.row_groups = (p.rho + rows - 1) / rows;
   const int64_t grid = (int64_t)p.n_items * p.Hkv * p.row_groups;
   if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;

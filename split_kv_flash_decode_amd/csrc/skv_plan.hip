@@ -11,8 +11,8 @@
 //  1. counts: an explicit count, or the work floor ceil(span * R / work),
 //     clamped to [1, min(max_partitions, tiles of the span)];
 //  2. without an explicit count, a batch that does not fill the base budget
-//     num_cus * ctas_per_cu / Hkv raises each request to its span share of
-//     it (at most span / min_tokens, at most the clamp);
+//     num_cus * ctas_per_cu / (Hkv * workgroups_per_head) raises each request
+//     to its span share of it (at most span / min_tokens, at most the clamp);
 //  3. counts above the capacity are scaled down (at least 1 each), then the
 //     first largest is trimmed until the sum fits;
 //  4. header, counts, exclusive prefix sums (record slots) and the work list:
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanDev h, const int32_t
 
   // 2. raise to the base budget
   if (h.explicit_p <= 0 && tot > 0) {
-    const int64_t budget = (int64_t)h.cus * h.ctas / h.Hkv;
+    const int64_t budget = (int64_t)h.cus * h.ctas / ((int64_t)h.Hkv * h.wph);
     if (sum < budget) {
       int64_t s2 = 0;
       for (int b = tid; b < B; b += kThreads) {

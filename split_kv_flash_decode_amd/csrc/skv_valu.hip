@@ -21,7 +21,7 @@ namespace skv {
 
 namespace {
 
-constexpr int RC = 8;   // query rows per wave
+constexpr int RC = kValuRows;   // query rows per wave
 
 template <class QT>
 __device__ __forceinline__ float load_q(const void* q, int64_t idx) {

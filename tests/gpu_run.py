@@ -56,8 +56,7 @@ def bench_step(p, impl: str = "auto", ws_fill: Optional[float] = None):
     Returns (o, workspace, plan)."""
     s = p.spec
     d, a, o = desc_args(p, impl)
-    ph = skv.plan_hints(s.B, s.R, s.Hkv, causal=s.causal, window=s.window,
-                        partitions_per_request=s.partitions_per_request)
+    ph = skv.plan_hints_for(d, True, partitions_per_request=s.partitions_per_request)
     plan = skv.Plan(ph, list(s.ctx), p.device)
     ws = skv.Workspace(d, plan.info.slots, p.device, fill=ws_fill)
     plan.refresh(list(s.ctx))

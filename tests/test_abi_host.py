@@ -245,3 +245,36 @@ def test_device_plan_refresh_fails_closed_on_the_host():
                                      skv.plan_meta_len(4097, 8192), None) == -6
     bad = skv.plan_hints(4, 0, 1)
     assert L.skv_plan_refresh_device(ctypes.byref(bad), fake, 8, fake, n, None) == -8
+
+
+def test_plan_hints_for_desc_follow_the_kernel_family():
+    # matrix-core kernel: one workgroup per CU, one per group of 64 (32 at D 256) rows
+    h = skv.plan_hints_for(_desc(B=2, R=4, Hq=16, Hkv=1, D=128))            # bf16 Q, fp8 KV, rho 64
+    assert (h.batch, h.q_rows, h.num_kv_heads, h.causal) == (2, 4, 1, 1)
+    assert (h.ctas_per_cu, h.workgroups_per_head, h.min_tokens_per_partition) == (1, 1, 0)
+    h = skv.plan_hints_for(_desc(B=1, R=16, Hq=24, Hkv=4, D=256, kdt=torch.int8))   # rho 96 at D 256
+    assert (h.ctas_per_cu, h.workgroups_per_head) == (1, 3)
+    h = skv.plan_hints_for(_desc(B=1, R=4, Hq=40, Hkv=2, D=128, kdt=torch.int8))    # rho 80
+    assert h.workgroups_per_head == 2
+    # vector kernel (fp32 Q): one-wave workgroups of 8 rows, tile-sized partitions
+    h = skv.plan_hints_for(_desc(B=1, R=1, Hq=14, Hkv=2, D=64, qdt=torch.float32, kdt=torch.float32))
+    assert (h.ctas_per_cu, h.workgroups_per_head, h.min_tokens_per_partition) == (16, 1, 64)
+    h = skv.plan_hints_for(_desc(R=4, Hq=16, Hkv=1, bs=8))                  # page 8: vector kernel
+    assert (h.ctas_per_cu, h.workgroups_per_head) == (16, 8)
+    bad = _desc()
+    bad.head_dim = 96
+    assert skv.lib().skv_plan_hints_for_desc(ctypes.byref(bad), 1, ctypes.byref(skv.PlanHints())) == -2
+
+
+def test_planner_budget_counts_workgroups_per_head():
+    # int8 verifier: B1, R16, Hkv 4, three row groups -> 256 / (4 * 3) = 21 partitions
+    _, info, _ = _plan([20676], R=16, Hkv=4, ctas_per_cu=1, workgroups_per_head=3)
+    assert info.num_items == 21
+    # the same without row groups: 256 / 4 = 64, then 20676 / 256 = 80 keys-limited -> 64
+    _, info, _ = _plan([20676], R=16, Hkv=4, ctas_per_cu=1)
+    assert info.num_items == 64
+    # the page's example is unchanged: B200 x 200k MTP4 -> 16 per request
+    _, info, cap = _plan([200000] * 200, R=4, Hkv=1, ctas_per_cu=1, workgroups_per_head=1)
+    assert info.num_items == 3200 and info.max_partitions == 16 and cap == 3200
+    with pytest.raises(skv.SkvError):
+        _plan([100], workgroups_per_head=-1)

@@ -66,6 +66,23 @@ def test_planned_matches_oracle(n):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_planned_with_descriptor_hints_matches_oracle(n):
+    """The planner with skv_plan_hints_for_desc (the kernel family's budget)."""
+    from tests.gpu_run import desc_args
+    import split_kv_flash_decode_amd as skv
+    p = _problem(n, seed=25 + n)
+    s = p.spec
+    d, a, o = desc_args(p)
+    h = skv.plan_hints_for(d, True, partitions_per_request=s.partitions_per_request)
+    plan = skv.Plan(h, list(s.ctx), p.device)
+    ws = skv.Workspace(d, plan.info.slots, p.device, fill=float("nan"))
+    skv.attention_decode_paged_planned(d, a, plan.dev, plan.capacity, ws)
+    torch.cuda.synchronize()
+    print("plan", plan.info.num_items, plan.info.max_partitions, flush=True)
+    _check(p, o, n, f"cfg{n} planned, descriptor hints")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_sharp_variant(n):
     p = _problem(n, seed=30 + n, q_mult=8.0)
     for impl in IMPLS[n]:

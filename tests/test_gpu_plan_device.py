@@ -48,13 +48,16 @@ def _cases():
     out.append(("verifier16", dict(q_rows=16, num_kv_heads=4), [20676], None))
     out.append(("batched_decode", dict(q_rows=1, num_kv_heads=8, causal=False), [4096] * 32, None))
     out.append(("with_empty", dict(q_rows=1, num_kv_heads=2, causal=False), [0, 1, 63, 64, 65, 5000, 0], None))
+    out.append(("verifier16_row_groups", dict(q_rows=16, num_kv_heads=4, ctas_per_cu=1, workgroups_per_head=3),
+                [20676], None))
     for i in range(12):
         B = int(rng.choice([1, 3, 17, 128, 600, 2048]))
         R = int(rng.choice([1, 4, 16]))
         ctx = [int(x) for x in rng.choice([0, 1, 37, 512, 3000, 40000, 250000], size=B)]
         kw = dict(q_rows=R, num_kv_heads=int(rng.choice([1, 2, 8])), causal=R > 1,
                   window=int(rng.choice([0, 0, 700])), max_partitions=int(rng.choice([0, 8, 64])),
-                  min_tokens_per_partition=int(rng.choice([0, 128, 1024])))
+                  min_tokens_per_partition=int(rng.choice([0, 128, 1024])),
+                  ctas_per_cu=int(rng.choice([0, 1, 16])), workgroups_per_head=int(rng.choice([0, 1, 3])))
         if i % 4 == 3:
             kw["partitions_per_request"] = int(rng.integers(1, 40))
         out.append((f"random{i}_B{B}", kw, ctx, None))
