@@ -150,7 +150,7 @@ PAGE_TABLE = [
 
 
 def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f32",
-                mode: str = "two_stage"):
+                mode: str = "two_stage", event_free_pass: bool = False):
     """Generate the workload, run the planned step (host plan refresh, metadata
     copy, partial, combine) ``warmup`` + ``steps`` times; returns
     (ms per step, partial ms list, combine ms list, plan, problem).
@@ -158,7 +158,12 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     ``mode`` "fused": the single-kernel split + merge instead of partial +
     combine (its time is reported as the partial time, combine 0);
     "device_plan": the plan refreshed on the GPU from the device lengths
-    instead of on the host."""
+    instead of on the host. In the timed steps only the partial kernel is
+    bracketed by events (each event record adds a few microseconds to the
+    stream); the combine's time comes from a few extra steps afterwards.
+    ``event_free_pass``: the time per step comes from a first timed pass
+    without any event (on short steps even two records per step are a
+    visible share), the kernel times from a second pass with events."""
     import torch
 
     import split_kv_flash_decode_amd as skv
@@ -196,13 +201,20 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
             if ev is not None:
                 ev[1].record(stream)
             skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
-        if ev is not None:
+        if ev is not None and len(ev) > 2:
             ev[2].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    plain_ms = None
+    if event_free_pass:
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step()
+        torch.cuda.synchronize()
+        plain_ms = (time.perf_counter() - t0) * 1e3 / steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
@@ -210,8 +222,12 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     part_ms = [e[0].elapsed_time(e[1]) for e in events]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
-    return wall * 1e3 / steps, part_ms, comb_ms, plan, p
+    extra = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(min(steps, 10))]
+    for e in extra:
+        step(e)
+    torch.cuda.synchronize()
+    comb_ms = [e[1].elapsed_time(e[2]) for e in extra]
+    return (plain_ms if event_free_pass else wall * 1e3 / steps), part_ms, comb_ms, plan, p
 
 
 def table(args) -> int:
@@ -223,7 +239,7 @@ def table(args) -> int:
         spec = config_spec(n, block_size=bs, v_layout=vl, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup)
+        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, event_free_pass=True)
         tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
         print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
                           "effective_TBps": round(tbs, 3), "page_us_per_step": page_us,
@@ -263,7 +279,8 @@ def next_rows(args) -> int:
         spec = config_spec(n, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, record_dtype=rec, mode=mode)
+        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, record_dtype=rec, mode=mode,
+                                                    event_free_pass=True)
         part_us = sum(part_ms) / len(part_ms) * 1e3
         unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
         alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
