@@ -131,9 +131,9 @@ extern "C" {
 /* The planner's default cap on partitions per request (max_partitions = 0):
  * a merge visits every record of a request, so past this many partitions
  * the merge costs more than the extra partial workgroups save (measured on
- * one 200,000-key request with fifteen of 1,024). An explicit
+ * one 100,000- or 200,000-key request with fifteen of 1,024). An explicit
  * max_partitions up to SKV_MAX_SPLITS still applies. */
-#define SKV_PLAN_DEFAULT_MAX_PARTITIONS 128
+#define SKV_PLAN_DEFAULT_MAX_PARTITIONS 160
 
 /* Status codes. */
 #define SKV_OK 0

@@ -170,7 +170,7 @@ def test_planner_budget_floor_for_small_batches():
     # intro of the same page: the base budget is two workgroups per CU (512 on 256 CUs)
     meta, info, cap = _plan([200000] + [1024] * 15)
     B, C, n, pmax, P, slot0, work = _decode(meta)
-    assert P[0] == 128                                    # the long request takes the budget, capped
+    assert P[0] == 160                                    # the long request takes the budget, capped
     meta, info, cap = _plan([200000] + [1024] * 15, max_partitions=256)
     assert _decode(meta)[4][0] == 256                     # an explicit cap up to the maximum of 256
     assert all(2 <= p <= 4 for p in P[1:])
