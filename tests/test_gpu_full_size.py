@@ -8,7 +8,9 @@ first, a middle and the last of 200 requests of 200,000 keys; config 5: the
 the host with only the pages its table row references. Same tolerance as the
 reduced-shape tests: |d| <= 5e-3 + 5e-3 |ref|, rel-L2 <= 1e-2, row cosine >=
 0.9999. Scratch records start NaN-filled, so a record the combine reads but no
-partial wrote shows up as NaN.
+partial wrote shows up as NaN. The uniform split counts the workloads name
+(single request 1, 2, 4, 8; verifier 2, 4, 8) run at full size too, whole
+output, both kernel families.
 """
 
 from __future__ import annotations
@@ -46,3 +48,19 @@ def test_full_size_bench_step_matches_oracle(n):
         del p, o, ws, plan
         gc.collect()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n,S", [(1, 1), (1, 2), (1, 4), (1, 8), (3, 2), (3, 4), (3, 8)])
+def test_full_size_uniform_split_counts(n, S):
+    """The split counts the workloads name (single request: 1, 2, 4, 8;
+    verifier: 2, 4, 8) at full size, both kernel families, whole output."""
+    from tests.gpu_run import run
+    spec = config_spec(n)
+    p = make_problem(spec, seed=40 + S, device="cuda")
+    ref = oracle_output(p)
+    impls = ["valu"] if spec.q_dtype == "f32" else ["valu", "mfma"]
+    for impl in impls:
+        o, _, _ = run(p, "split", num_splits=S, impl=impl, ws_fill=float("nan"))
+        st = compare(to_f64(o), ref, "f32" if spec.kv_dtype == "f32" else "lowp")
+        print(f"[full cfg{n} S={S} {impl}] {st}", flush=True)
+        assert st["ok"], (n, S, impl, st)
