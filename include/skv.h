@@ -111,8 +111,11 @@
  * The merge ([DR] Design, Q3; [PA] Changes): M = max over splits with l > 0
  * (and the sink logit in log2 units); L = sum_s 2^(m_s - M) l_s
  * (+ 2^(sink log2(e) - M)); O = (sum_s 2^(m_s - M) acc_s) * (1 / (L + 1e-9)),
- * splits taken in increasing s. With one split and fp32 records this is
- * bit-identical to the single-pass entry points.
+ * splits taken in increasing s. A merge of one record is exactly the
+ * single-pass finalization, so a request with one split (num_splits = 1, or
+ * P_b = 1 in a plan) gets its output from the partial stage directly, with
+ * the same bits as the single-pass entry points, writes no record, and the
+ * combine stage leaves it alone.
  */
 #ifndef SKV_H_
 #define SKV_H_
@@ -333,7 +336,8 @@ int skv_attention_decode_paged_planned(const skv_desc* d, const skv_args* a,
 
 /* ---- the two stages on their own -----------------------------------------
  * skv_splitkv_partial enqueues only the partial kernel, skv_splitkv_combine
- * only the combine kernel; a split-KV call is exactly the two in order.
+ * only the combine kernel; a split-KV call is exactly the two in order. The
+ * partial stage writes o for requests with one split (see the merge above).
  * plan_meta NULL selects uniform splits (num_splits); otherwise num_splits
  * must be the plan's capacity C. */
 int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,

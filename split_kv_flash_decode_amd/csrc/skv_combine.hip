@@ -10,8 +10,10 @@
 // are 16-byte coalesced and a request with many splits is read by many
 // lanes at once. The quarters are visited in a fixed order, which makes the
 // result deterministic, and with one split bit-identical to the single-pass
-// kernels (same operations as finalize_one). bf16 records are widened to
-// fp32 as they are read; the arithmetic is the same.
+// kernels (same operations as finalize_one); requests with one split are
+// therefore finalized by the partial kernels themselves and skipped here.
+// bf16 records are widened to fp32 as they are read; the arithmetic is the
+// same.
 
 #include "skv_device.h"
 
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Params p) {
     S = p.num_splits;
     slot0 = b * S;
   }
+  if (S == 1) return;                             // the partial kernel wrote it
   int j, h;
   row_jh(p, g, r, &j, &h);
   const floatx4 v = merge_splits4<RBF>(p, g, r, d, h, S, slot0, q);

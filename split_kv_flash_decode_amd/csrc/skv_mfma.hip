@@ -914,7 +914,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     return v;
   };
 
-  if (p.finalize) {
+  // A request with one split writes its output here (the merge of one record
+  // is exactly this finalize, so the result is the same bits) and the
+  // combine skips it.
+  if (p.finalize || it.S == 1) {
     for (int idx = tid; idx < nrow * (D / 4); idx += NT) {
       const int rr = idx / (D / 4), d = 4 * (idx - rr * (D / 4));
       const int r = rbase + rr;

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
     __syncthreads();
   }
 
-  if (p.finalize) {
+  if (p.finalize || it.S == 1) {                 // one split: the output itself (combine skips it)
 #pragma unroll
     for (int rr = 0; rr < RC; ++rr) {
       const int r = r0 + rr;
