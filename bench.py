@@ -163,7 +163,13 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     stream); the combine's time comes from a few extra steps afterwards.
     ``event_free_pass``: the time per step comes from a first timed pass
     without any event (on short steps even two records per step are a
-    visible share), the kernel times from a second pass with events."""
+    visible share), the kernel times from a second pass with events; a third
+    pass times each step alone (events around the step) after a 1 GiB buffer
+    write has pushed the inputs out of L2 and the 256 MB last-level cache
+    (``cold_ms``, the median): the cache-cold time of workloads small enough
+    to stay cache-resident between back-to-back steps.
+    Returns (ms per step, partial ms list, combine ms list, plan, problem,
+    cold ms or None)."""
     import torch
 
     import split_kv_flash_decode_amd as skv
@@ -227,7 +233,21 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
         step(e)
     torch.cuda.synchronize()
     comb_ms = [e[1].elapsed_time(e[2]) for e in extra]
-    return (plain_ms if event_free_pass else wall * 1e3 / steps), part_ms, comb_ms, plan, p
+    cold_ms = None
+    if event_free_pass:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        times = []
+        for k in range(min(steps, 50)):
+            flush.fill_(float(k))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        cold_ms = sorted(times)[len(times) // 2]
+        del flush
+    return (plain_ms if event_free_pass else wall * 1e3 / steps), part_ms, comb_ms, plan, p, cold_ms
 
 
 def table(args) -> int:
@@ -239,10 +259,13 @@ def table(args) -> int:
         spec = config_spec(n, block_size=bs, v_layout=vl, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, event_free_pass=True)
+        ms, part_ms, comb_ms, plan, p, cold_ms = timed_steps(spec, n, steps, warmup, event_free_pass=True)
         tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
         print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
-                          "effective_TBps": round(tbs, 3), "page_us_per_step": page_us,
+                          "effective_TBps": round(tbs, 3),
+                          "us_per_step_cache_cold": round(cold_ms * 1e3, 2),
+                          "effective_TBps_cache_cold": round(spec_bytes(spec) / (cold_ms * 1e-3) / 1e12, 3),
+                          "page_us_per_step": page_us,
                           "page_TBps": page_tbs, "time_vs_page": round(ms * 1e3 / page_us, 4),
                           "partial_us_mean": round(sum(part_ms) / len(part_ms) * 1e3, 2),
                           "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
@@ -279,12 +302,13 @@ def next_rows(args) -> int:
         spec = config_spec(n, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p = timed_steps(spec, n, steps, warmup, record_dtype=rec, mode=mode,
-                                                    event_free_pass=True)
+        ms, part_ms, comb_ms, plan, p, cold_ms = timed_steps(spec, n, steps, warmup, record_dtype=rec,
+                                                             mode=mode, event_free_pass=True)
         part_us = sum(part_ms) / len(part_ms) * 1e3
         unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
         alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
         row = {"row": name, "workload": workload_name(spec), "us_per_step": round(ms * 1e3, 2),
+               "us_per_step_cache_cold": round(cold_ms * 1e3, 2),
                "effective_TBps": round(spec_bytes(spec) / (ms * 1e-3) / 1e12, 3),
                "partial_us_mean": round(part_us, 2),
                "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
@@ -357,7 +381,7 @@ def main(argv=None) -> int:
     spec = config_spec(args.config, **overrides)
     print(f"[bench] generating {spec.name} on cuda:0 and timing ...", file=sys.stderr, flush=True)
     t = time.time()
-    ms_per_step, part_ms, comb_ms, plan, p = timed_steps(spec, args.seed, args.steps, args.warmup)
+    ms_per_step, part_ms, comb_ms, plan, p, _ = timed_steps(spec, args.seed, args.steps, args.warmup)
     print(f"[bench] done in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     nbytes = spec_bytes(spec)
     tbs = nbytes / (ms_per_step * 1e-3) / 1e12
