@@ -64,7 +64,7 @@
  *   ctx_lens      int32 [B] device visible lengths (the keys of a request,
  *                 its R query tokens included)
  *   sinks         fp32 [Hq] per-query-head sink logits (natural-log units)
- *   tree_mask     uint64 [B][R] verify masks (optional, see below)
+ *   tree_mask     uint64 [B][R][ceil(R / 64)] verify masks (optional, see below)
  *
  * Semantics (readings of the pages, see the design notes of the repository)
  *   Query head h uses KV head h / (Hq / Hkv). Causal row j of a request of
@@ -79,12 +79,14 @@
  * reading here): the R query tokens of a causal request are the draft tokens
  * at keys ctx - R .. ctx - 1, in an order where every token comes after its
  * ancestors. With args.tree_mask set, row j sees the committed prefix
- * t < ctx - R as before, and draft key ctx - R + i only when bit i of
- * tree_mask[b * R + j] is set (and i <= j: a row never sees a later draft).
+ * t < ctx - R as before, and draft key ctx - R + i only when bit i % 64 of
+ * word tree_mask[(b * R + j) * W + i / 64] is set, W = ceil(R / 64) (and
+ * i <= j: a row never sees a later draft; a window still applies on top).
  * Causal verification is the mask with bits 0..j set; tree verification sets
  * the bits of the token's ancestors and itself; independent-batch
- * verification sets bit j alone. Requires causal = 1, window = 0 and R <= 64
- * (SKV_ERR_UNSUPPORTED otherwise). Split ranges and records are unchanged.
+ * verification sets bit j alone. Requires causal = 1 and
+ * R <= SKV_MAX_VERIFY_ROWS (SKV_ERR_UNSUPPORTED otherwise). Split ranges and
+ * records are unchanged.
  *
  * Split ranges ([DR] Design; [PA] Changes). For a request with S splits the
  * split range is [u, ctx) where u = 0, or with a window the earliest row's
@@ -131,6 +133,7 @@ extern "C" {
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
 #define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
+#define SKV_MAX_VERIFY_ROWS 256   /* query rows per request with verify masks (four mask words) */
 /* The planner's default cap on partitions per request (max_partitions = 0):
  * a merge visits every record of a request, so past this many partitions
  * the merge costs more than the extra partial workgroups save (measured on
@@ -200,7 +203,7 @@ typedef struct skv_args {
   const int32_t* ctx_lens;
   const float* sinks;
   void* o;
-  const uint64_t* tree_mask;   /* NULL, or [B][R] verify masks (see above) */
+  const uint64_t* tree_mask;   /* NULL, or [B][R][ceil(R / 64)] verify masks (see above) */
 } skv_args;
 
 /* Caller-owned partial-record buffers (device memory), sized by

@@ -128,8 +128,9 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
 
     Two-pass softmax in float64 over the gathered, dequantized cache. Returns a
     float64 array [len(requests)][R][Hq][D] (all requests by default). With
-    ``arrays["tree_mask"]`` (int64 [B][R] bit patterns) the visible keys of a
-    causal row are further restricted by its verify mask (``verify_keys``).
+    ``arrays["tree_mask"]`` (int64 [B][R] or [B][R][W] bit patterns, word k
+    holding drafts 64k .. 64k + 63) the visible keys of a causal row are
+    further restricted by its verify mask (``verify_keys``).
     """
     q = decode_storage(arrays["q"], q_dtype)
     ctx = np.asarray(arrays["ctx"], dtype=np.int64)
@@ -150,7 +151,9 @@ def decode_attention(arrays: dict, *, R: int, Hq: int, Hkv: int, D: int, causal:
             lo, hi = visible_range(n, R, j, causal, window)
             keys = np.arange(lo, hi)
             if tree is not None:
-                keys = verify_keys(n, R, j, int(tree[b, j]) & ((1 << 64) - 1), lo, hi)
+                words = np.asarray(tree[b, j]).reshape(-1)          # [W] 64-bit words, word k = drafts 64k..
+                mask = sum((int(w) & ((1 << 64) - 1)) << (64 * k) for k, w in enumerate(words))
+                keys = verify_keys(n, R, j, mask, lo, hi)
             if keys.size == 0:
                 continue                                   # no visible key: O = 0
             for g in range(Hkv):

@@ -18,11 +18,12 @@ device the problem is built on, in this order):
 6. A random permutation of the P pool pages; request b takes the next
    ceil(ctx_b / bs) of them as its logical pages 0, 1, ...  P is
    max(N + 1, ceil(1.25 N)) for N referenced pages, so spare pages exist.
-7. Verify masks (``spec.verify`` other than "causal"), int64 [B][R]: "chain"
-   sets bits 0..j of row j; "independent" bit j alone; "tree" draws, per
-   request, a parent for each draft i (uniform over the prefix root and the
-   drafts 0..i-1, one torch.randint per draft) and sets the bits of i and its
-   ancestors.
+7. Verify masks (``spec.verify`` other than "causal"), int64 [B][R][W] with
+   W = ceil(R / 64) words per row (bit i % 64 of word i / 64 = draft i):
+   "chain" sets bits 0..j of row j; "independent" bit j alone; "tree" draws,
+   per request, a parent for each draft i (uniform over the prefix root and
+   the drafts 0..i-1, one torch.randint per draft) and sets the bits of i
+   and its ancestors.
 
 Poison (``spec.poison``): every spare pool page, and every slot of a request's
 last page at or beyond its context length, is filled with NaN (fp32/bf16),
@@ -63,7 +64,7 @@ class Problem:
     ctx: torch.Tensor                  # int32 [B]
     sinks: Optional[torch.Tensor]      # fp32 [Hq]
     kv_capacity: int                   # contiguous tokens per (request, KV head)
-    tree_mask: Optional[torch.Tensor] = None   # int64 [B][R] verify masks
+    tree_mask: Optional[torch.Tensor] = None   # int64 [B][R][ceil(R / 64)] verify masks
 
     @property
     def device(self) -> torch.device:
@@ -202,10 +203,11 @@ def make_problem(spec: ProblemSpec, seed: int, device="cpu", paged: bool = True,
 
 
 def verify_masks(spec: ProblemSpec, g: torch.Generator) -> torch.Tensor:
-    """int64 [B][R] verify masks of ``spec.verify`` (recipe step 7); bit i of
-    row j: draft i is visible to row j."""
+    """int64 [B][R][W] verify masks of ``spec.verify`` (recipe step 7); bit i
+    of row j: draft i is visible to row j."""
     B, R = spec.B, spec.R
-    assert R <= 64
+    W = (R + 63) // 64
+    assert R <= 256
     rows = []
     for _ in range(B):
         m = []
@@ -220,7 +222,11 @@ def verify_masks(spec: ProblemSpec, g: torch.Generator) -> torch.Tensor:
             else:
                 raise ValueError(spec.verify)
             m.append(w)
-        rows.append([w - (1 << 64) if w >= 1 << 63 else w for w in m])   # as int64 bits
+        words = []
+        for w in m:
+            ws = [(w >> (64 * k)) & ((1 << 64) - 1) for k in range(W)]
+            words.append([x - (1 << 64) if x >= 1 << 63 else x for x in ws])   # as int64 bits
+        rows.append(words)
     return torch.tensor(rows, dtype=torch.int64)
 
 

@@ -216,8 +216,11 @@ def make_args(q, k, v, ctx_lens, o, *, k_scale=None, v_scale=None, page_table=No
     a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
     a.page_table, a.ctx_lens, a.sinks = _ptr(page_table), _ptr(ctx_lens), _ptr(sinks)
     if tree_mask is not None:
-        _need(tree_mask.dtype in (torch.int64, torch.uint64) and tuple(tree_mask.shape) == tuple(q.shape[:2]),
-              "tree_mask must be a 64-bit integer [B][R] tensor")
+        B, R = q.shape[:2]
+        W = (R + 63) // 64
+        ok = tuple(tree_mask.shape) == (B, R, W) or (W == 1 and tuple(tree_mask.shape) == (B, R))
+        _need(tree_mask.dtype in (torch.int64, torch.uint64) and ok,
+              "tree_mask must be a 64-bit integer [B][R][ceil(R/64)] tensor ([B][R] when R <= 64)")
         a.tree_mask = _ptr(tree_mask)
     return a
 

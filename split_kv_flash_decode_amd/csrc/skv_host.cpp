@@ -64,7 +64,7 @@ int check_args(const skv_desc* d, const skv_args* a, int paged) {
   bool quant = d->kv_dtype == SKV_INT8 || d->kv_dtype == SKV_FP8_E4M3;
   if (quant && (!a->k_scale || !a->v_scale)) return SKV_ERR_NULL;
   if (d->has_sink && !a->sinks) return SKV_ERR_NULL;
-  if (a->tree_mask && (d->causal != 1 || d->window != 0 || d->q_rows > 64)) return SKV_ERR_UNSUPPORTED;
+  if (a->tree_mask && (d->causal != 1 || d->q_rows > SKV_MAX_VERIFY_ROWS)) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 

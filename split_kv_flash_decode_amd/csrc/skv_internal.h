@@ -20,7 +20,7 @@ struct Params {
   const int32_t* ctx;
   const float* sinks;
   void* o;
-  const uint64_t* tree_mask;  // verify masks [B][R], or nullptr
+  const uint64_t* tree_mask;  // verify masks [B][R][ceil(R / 64)], or nullptr
   float* pm;
   float* pl;
   void* pacc;            // fp32 or (rec_bf16) bf16 record accumulators
@@ -109,11 +109,26 @@ SKV_HD void split_range(int ctx, int R, int causal, int window, int S, int s, in
 }
 
 // Visible key range [vlo, vhi) of query row j.
-// Bit of a verify mask for key t of a row (draft keys start at dbase =
-// ctx - R; the prefix is always visible). The shift count is wrapped so that
-// keys past ctx, which other tests mask, stay defined.
-SKV_HD bool tree_visible(uint64_t mask, int t, int dbase) {
-  return t < dbase || ((mask >> ((unsigned)(t - dbase) & 63u)) & 1ull) != 0;
+// Words of a row's verify mask.
+SKV_HD int verify_words(int R) { return (R + 63) >> 6; }
+
+// Bit of a verify mask for key t of a row whose (up to four) words are w
+// (draft keys start at dbase = ctx - R; the prefix is always visible). Word
+// and shift are clamped so that keys past ctx, which other tests mask, stay
+// defined.
+SKV_HD bool tree_visible(const uint64_t (&w)[4], int t, int dbase) {
+  if (t < dbase) return true;
+  const unsigned i = (unsigned)(t - dbase);
+  const unsigned q = i >> 6;
+  const uint64_t x = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
+  return ((x >> (i & 63u)) & 1ull) != 0;
+}
+
+// The same, reading the row's words from memory (only for keys past dbase).
+SKV_HD bool tree_visible_mem(const uint64_t* row, int t, int dbase) {
+  if (t < dbase) return true;
+  const unsigned i = (unsigned)(t - dbase);
+  return ((row[(i >> 6) & 3u] >> (i & 63u)) & 1ull) != 0;
 }
 
 SKV_HD void row_range(int ctx, int R, int causal, int window, int j, int* vlo, int* vhi) {

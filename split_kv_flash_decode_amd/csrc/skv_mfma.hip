@@ -291,10 +291,15 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
   const int wrow0 = rbase + 32 * rh;
   int vlo = 0, vhi = 0;
-  uint64_t tmask = ~0ull;                        // TM: this lane's row's verify mask
+  uint64_t tmask[4] = {~0ull, ~0ull, ~0ull, ~0ull};   // TM: this lane's row's verify mask words
   if (wrow0 + i32 < p.rho) {
     row_range(ctx, p.R, p.causal, p.window, (wrow0 + i32) / p.G, &vlo, &vhi);
-    if constexpr (TM) tmask = p.tree_mask[(int64_t)b * p.R + (wrow0 + i32) / p.G];
+    if constexpr (TM) {
+      const int nw = verify_words(p.R);
+      const uint64_t* mrow = p.tree_mask + ((int64_t)b * p.R + (wrow0 + i32) / p.G) * nw;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) tmask[w] = w < nw ? mrow[w] : 0ull;
+    }
   }
   // with verify masks, blocks reaching the draft keys take the masked path
   const int dbase = TM ? ctx - p.R : 0x7FFFFFFF;

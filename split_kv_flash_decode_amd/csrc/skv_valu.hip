@@ -121,16 +121,16 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
     q_s[rr][d] = x;
   }
   int vlo[RC], vhi[RC];
-  uint64_t tm[RC];                              // verify masks (all ones without)
+  const uint64_t* tm[RC];                       // rows' verify mask words (with masks)
   const int dbase = p.tree_mask ? ctx - p.R : 0x7FFFFFFF;
 #pragma unroll
   for (int rr = 0; rr < RC; ++rr) {
     vlo[rr] = 0;
     vhi[rr] = 0;
-    tm[rr] = ~0ull;
+    tm[rr] = p.tree_mask;
     if (r0 + rr < p.rho) {
       row_range(ctx, p.R, p.causal, p.window, (r0 + rr) / p.G, &vlo[rr], &vhi[rr]);
-      if (p.tree_mask) tm[rr] = p.tree_mask[(int64_t)b * p.R + (r0 + rr) / p.G];
+      if (p.tree_mask) tm[rr] = p.tree_mask + ((int64_t)b * p.R + (r0 + rr) / p.G) * verify_words(p.R);
     }
   }
   float m[RC], l[RC], acc[RC][DPL];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
 #pragma unroll
     for (int rr = 0; rr < RC; ++rr) {
       float x = sc[rr] * ksc * p.scale_log2;
-      const bool vis = valid && t >= vlo[rr] && t < vhi[rr] && tree_visible(tm[rr], t, dbase);
+      const bool vis = valid && t >= vlo[rr] && t < vhi[rr] && tree_visible_mem(tm[rr], t, dbase);
       x = vis ? x : -INFINITY;
       const float mt = wave_max(x);
       const float mn = fmaxf(m[rr], mt);

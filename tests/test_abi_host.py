@@ -114,12 +114,11 @@ def test_compute_calls_fail_closed_without_launching():
         assert isinstance(skv.status_str(s), str) and skv.status_str(s)
 
 
-def test_verify_masks_need_causal_rows_without_window():
+def test_verify_masks_need_causal_rows_up_to_the_maximum():
     L = skv.lib()
     fake = 1 << 20                                        # never dereferenced: the call fails first
-    for kw, setup in ((dict(), lambda d: setattr(d, "window", 8)),
-                      (dict(), lambda d: setattr(d, "causal", 0)),
-                      (dict(R=65), lambda d: None)):
+    for kw, setup in ((dict(), lambda d: setattr(d, "causal", 0)),
+                      (dict(R=257, Hq=4), lambda d: None)):
         d = _desc(**kw)
         setup(d)
         a = skv.Args(fake, fake, fake, fake, fake, fake, fake, None, fake, fake)

@@ -8,8 +8,9 @@ and the drafts its mask word lets through (never one after itself). Seeded
 masks: "chain" (must equal the plain causal call bitwise), "independent" (bit
 j alone) and random trees (a parent per draft, the bits of its ancestors).
 Both kernel families, uniform splits, the planner, the fused call, the sharp
-variant, 64 draft rows, contexts shorter than R. Bar: the low-precision
-tolerance (|d| <= 5e-3 + 5e-3 |ref|, rel-L2 1e-2, row cosine 0.9999).
+variant, windows and sinks, 64 to 256 draft rows (one to four mask words per
+row), contexts shorter than R. Bar: the low-precision tolerance
+(|d| <= 5e-3 + 5e-3 |ref|, rel-L2 1e-2, row cosine 0.9999).
 """
 
 from __future__ import annotations
@@ -41,6 +42,10 @@ CASES = [
     ("cfg4_tree_short_ctx", 4, dict(verify="tree", ctx=(3, 4, 2000))),
     ("cfg4_tree_sharp", 4, dict(verify="tree", q_mult=8.0)),
     ("cfg4_tree_t128", 4, dict(verify="tree", block_size=128, v_layout="transposed")),
+    ("cfg4_tree_window_sinks", 4, dict(verify="tree", window=300, sinks=True)),
+    ("cfg3_tree_r128", 3, dict(verify="tree", R=128, ctx=(900,))),
+    ("cfg3_independent_r256", 3, dict(verify="independent", R=256, ctx=(2300,))),
+    ("cfg4_tree_r200", 4, dict(verify="tree", R=200, ctx=(450, 1300, 205))),
 ]
 
 

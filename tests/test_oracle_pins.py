@@ -213,14 +213,21 @@ def test_identical_keys_give_mean_of_visible_values(ctx, R, causal, window, v_la
 
 
 def _as_int64_bits(words):
-    return np.array([[w - (1 << 64) if w >= 1 << 63 else w for w in row] for row in words], dtype=np.int64)
+    """Masks (Python ints, one per row) -> int64 [B][R][W] words, W = ceil(R / 64)."""
+    W = max(1, -(-len(words[0]) // 64))
+    def split(w):
+        ws = [(w >> (64 * k)) & ((1 << 64) - 1) for k in range(W)]
+        return [x - (1 << 64) if x >= 1 << 63 else x for x in ws]
+    return np.array([[split(w) for w in row] for row in words], dtype=np.int64)
 
 
-@pytest.mark.parametrize("ctx,R,kind", [
-    (23, 4, "independent"), (23, 4, "tree"), (64, 16, "tree"), (64, 16, "independent"),
-    (3, 4, "tree"), (4, 4, "independent"), (70, 64, "tree"), (70, 64, "high_bits"),
+@pytest.mark.parametrize("ctx,R,kind,window", [
+    (23, 4, "independent", 0), (23, 4, "tree", 0), (64, 16, "tree", 0), (64, 16, "independent", 0),
+    (3, 4, "tree", 0), (4, 4, "independent", 0), (70, 64, "tree", 0), (70, 64, "high_bits", 0),
+    (300, 130, "tree", 0), (300, 130, "independent", 0), (260, 256, "high_bits", 0), (100, 200, "tree", 0),
+    (64, 16, "tree", 9), (300, 130, "tree", 40), (70, 64, "independent", 100),
 ])
-def test_identical_keys_under_verify_masks_give_mean_of_visible_values(ctx, R, kind):
+def test_identical_keys_under_verify_masks_give_mean_of_visible_values(ctx, R, kind, window):
     """Equal logits: each row averages exactly the keys its mask lets through,
     so the position-coded column pins the visible set (prefix keys below
     ctx - R, the masked drafts, none after the row's own position)."""
@@ -230,21 +237,21 @@ def test_identical_keys_under_verify_masks_give_mean_of_visible_values(ctx, R, k
         if kind == "independent":
             w = 1 << i
         elif kind == "high_bits":                  # bits after the row: no effect
-            w = ((1 << 64) - 1) ^ ((1 << i) - 1) if i < 64 else 0
-            w &= (1 << 64) - 1
+            w = ((1 << R) - 1) ^ ((1 << i) - 1)
         else:
             par = int(rng.integers(-1, i)) if i > 0 else -1
             w = (words[par] if par >= 0 else 0) | (1 << i)
         words.append(w)
     arrays = _const_key_problem(ctx, R)
     arrays["tree_mask"] = _as_int64_bits([words])
-    out = oracle.decode_attention(arrays, R=R, Hq=2, Hkv=1, D=4, causal=True, window=0,
+    out = oracle.decode_attention(arrays, R=R, Hq=2, Hkv=1, D=4, causal=True, window=window,
                                   scale=0.5, q_dtype="f32", kv_dtype="f32", paged=True,
                                   block_size=5, v_layout="plain", has_sink=False)
     base = ctx - R
     for j in range(R):
-        vis = [t for t in range(0, max(base, 0))]
-        vis += [base + i for i in range(j + 1) if base + i >= 0 and (words[j] >> i) & 1]
+        lo = max(0, base + j - window + 1) if window else 0      # the window, on top of the mask
+        vis = [t for t in range(lo, max(base, 0))]
+        vis += [base + i for i in range(j + 1) if base + i >= max(lo, 0) and (words[j] >> i) & 1]
         if not vis:
             assert np.all(out[0, j] == 0)
             continue
