@@ -349,7 +349,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path needs no collectives; see the sharding notes in DESIGN.md)",
+              "(the path needs no collectives: requests and KV heads shard without exchange)",
               file=sys.stderr)
         return 2
 

@@ -148,7 +148,7 @@ extern "C" {
 #define SKV_ERR_DTYPE (-3)         /* unsupported dtype or dtype combination */
 #define SKV_ERR_SPLITS (-4)        /* num_splits < 1 or > SKV_MAX_SPLITS */
 #define SKV_ERR_CAPACITY (-5)      /* partial buffers hold too few records */
-#define SKV_ERR_UNSUPPORTED (-6)   /* valid request this build does not implement */
+#define SKV_ERR_UNSUPPORTED (-6)   /* valid request this library does not implement */
 #define SKV_ERR_LAUNCH (-7)        /* the HIP runtime rejected a kernel launch */
 #define SKV_ERR_PLAN (-8)          /* inconsistent plan hints or metadata sizes */
 #define SKV_ERR_ALIGN (-9)         /* partials.acc is not 16-byte aligned */

@@ -20,7 +20,7 @@ Sources (page titles and sections; no code is printed on any of them):
   the causal-window union and tile alignment (Changes), BF16 Q/O with FP8 KV
   and per-token FP32 scales (Performance).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * a request's context length counts its R query tokens; causal row j sits at
   position p_j = ctx - R + j and sees keys t <= p_j; a non-causal row sees all
