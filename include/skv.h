@@ -66,7 +66,7 @@
  *   sinks         fp32 [Hq] per-query-head sink logits (natural-log units)
  *   tree_mask     uint64 [B][R][ceil(R / 64)] verify masks (optional, see below)
  *
- * Semantics (readings of the pages, see the design notes of the repository)
+ * Semantics (readings of the pages where they leave a step open)
  *   Query head h uses KV head h / (Hq / Hkv). Causal row j of a request of
  *   length ctx sits at position p_j = ctx - R + j (non-causal rows: ctx - 1)
  *   and sees keys t in [0, ctx) with t <= p_j and, when window W > 0,
