@@ -50,16 +50,21 @@ def to_f64(o: torch.Tensor):
     return o.detach().double().cpu().numpy()
 
 
-def bench_step(p, impl: str = "auto", ws_fill: Optional[float] = None):
+def bench_step(p, impl: str = "auto", ws_fill: Optional[float] = None, record_dtype: str = "f32",
+               device_plan: bool = False):
     """The step ``bench.py`` times: plan (host) -> metadata copy -> partial -> combine,
     through splitkv_partial / splitkv_combine with the planner's capacity.
-    Returns (o, workspace, plan)."""
+    ``device_plan``: the metadata is overwritten with -1 and re-planned on the GPU
+    from the device lengths instead. Returns (o, workspace, plan)."""
     s = p.spec
-    d, a, o = desc_args(p, impl)
+    d, a, o = desc_args(p, impl, record_dtype=record_dtype)
     ph = skv.plan_hints_for(d, True, partitions_per_request=s.partitions_per_request)
     plan = skv.Plan(ph, list(s.ctx), p.device)
     ws = skv.Workspace(d, plan.info.slots, p.device, fill=ws_fill)
     plan.refresh(list(s.ctx))
+    if device_plan:
+        plan.dev.fill_(-1)
+        skv.plan_refresh_device(ph, p.ctx, plan.capacity, plan.dev)
     skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
     skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
     torch.cuda.synchronize()

@@ -10,7 +10,10 @@ reduced-shape tests: |d| <= 5e-3 + 5e-3 |ref|, rel-L2 <= 1e-2, row cosine >=
 0.9999. Scratch records start NaN-filled, so a record the combine reads but no
 partial wrote shows up as NaN. The uniform split counts the workloads name
 (single request 1, 2, 4, 8; verifier 2, 4, 8) run at full size too, whole
-output, both kernel families.
+output, both kernel families. So do the adjacent variants ``bench.py --next``
+times (fp16 Q/O, bf16 records, verify masks, the device plan refresh), in
+that same step, on the same samples; bf16 records add the bound of their own
+rounding (2^-8 times the oracle's output on |V|).
 """
 
 from __future__ import annotations
@@ -22,7 +25,7 @@ import torch
 
 from skvgen import config_spec, extract_request, make_problem
 from tests.gpu_run import bench_step, to_f64
-from tests.helpers import compare, oracle_output
+from tests.helpers import compare, oracle_abs_value_output, oracle_output
 
 pytestmark = pytest.mark.gpu
 
@@ -64,3 +67,36 @@ def test_full_size_uniform_split_counts(n, S):
         st = compare(to_f64(o), ref, "f32" if spec.kv_dtype == "f32" else "lowp")
         print(f"[full cfg{n} S={S} {impl}] {st}", flush=True)
         assert st["ok"], (n, S, impl, st)
+
+
+VARIANTS = [
+    ("cfg4_f16", 4, {"q_dtype": "f16"}, "f32", False),
+    ("cfg4_bf16_records", 4, {}, "bf16", False),
+    ("cfg4_tree_mask", 4, {"verify": "tree"}, "f32", False),
+    ("cfg4_device_plan", 4, {}, "f32", True),
+    ("cfg3_tree_mask", 3, {"verify": "tree"}, "f32", False),
+    ("cfg3_independent_mask", 3, {"verify": "independent"}, "f32", False),
+    ("cfg3_f16", 3, {"q_dtype": "f16"}, "f32", False),
+    ("cfg3_bf16_records_device_plan", 3, {}, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("name,n,over,rec,dev_plan", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_full_size_variant_rows_match_oracle(name, n, over, rec, dev_plan):
+    spec = config_spec(n, **over)
+    print(f"[full {name}] {spec.name}: B {spec.B}, keys {sum(spec.ctx)}", flush=True)
+    p = make_problem(spec, seed=14, device="cuda")
+    o, ws, plan = bench_step(p, ws_fill=float("nan"), record_dtype=rec, device_plan=dev_plan)
+    assert o.dtype == p.q.dtype
+    out = to_f64(o)
+    try:
+        for b in SAMPLES[n] or range(spec.B):
+            sub = extract_request(p, b)
+            extra = 2.0 ** -8 * oracle_abs_value_output(sub)[0] if rec == "bf16" else None
+            st = compare(out[b], oracle_output(sub)[0], "lowp", extra=extra)
+            print(f"[full {name} request {b} ctx {spec.ctx[b]}] {st}", flush=True)
+            assert st["ok"], (name, b, st)
+    finally:
+        del p, o, ws, plan
+        gc.collect()
+        torch.cuda.empty_cache()
