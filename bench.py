@@ -23,6 +23,9 @@ resident in HBM before timing starts. Prints one JSON line:
               committed measurement for the current kernel source exists
   cpu_baseline  the fp64 oracle timed on host cores over a bounded sample of
               the same workload (whole requests), as effective TB/s
+  copy_kernel  a 1 GiB device copy timed after the steps (bytes read plus
+              written per second): what a plain streaming kernel reaches on
+              this box, beside the published peak
 """
 
 from __future__ import annotations
@@ -99,6 +102,32 @@ def workload_name(spec) -> str:
             + (f", {spec.partitions_per_request} partitions/request" if spec.partitions_per_request else
                ", planner partitions")
             + (f", window {spec.window}" if spec.window else "") + (", sinks" if spec.sinks else ""))
+
+
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """A plain device-to-device copy of ``nbytes`` on the same stream, timed
+    with HIP events (median of three passes of ``reps`` copies): the box's own
+    streaming rate beside the 8 TB/s peak, counting bytes read plus written."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    rates = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        rates.append(2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GBps": round(sorted(rates)[1], 1), "bytes_per_copy": nbytes, "counted": "read + write",
+            "frac_of_peak": round(sorted(rates)[1] / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(problem, spec, budget_s: float = 12.0, max_requests: int = 200):
@@ -431,6 +460,7 @@ def main(argv=None) -> int:
         },
         "cpu_baseline": None,
     }
+    result["copy_kernel"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on host cores ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(p, spec, budget_s=args.cpu_budget)
