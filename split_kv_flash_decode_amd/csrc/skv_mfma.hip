@@ -271,7 +271,21 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   const int hh = lane >> 5;
   char* ring = smem + sid * NS * STAGE;
 
+  // Block order: the row groups of one (item, KV head) read the same keys.
+  // Workgroups are dealt to the eight XCDs (each with its own L2) in turn
+  // by block index, so consecutive indices would put those readers on
+  // different L2s; blocks 8 k + x of the first whole multiple of 8 tiles are
+  // therefore mapped so that every row group of a tile has the same x (one
+  // XCD, one L2), the rest in plain order.
   int blk = blockIdx.x;
+  if (p.row_groups > 1) {
+    const int RG = p.row_groups;
+    const int T8 = ((int)gridDim.x / RG) & ~7;
+    if (blk < T8 * RG) {
+      const int x = blk & 7, k = blk >> 3;
+      blk = ((k / RG) * 8 + x) * RG + k % RG;
+    }
+  }
   const int rg = blk % p.row_groups;
   blk /= p.row_groups;
   const int g = blk % p.Hkv;
