@@ -336,6 +336,21 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[db][v] = 0.0f;
+  // Register file of the accumulators. Two row halves (two waves per SIMD):
+  // arch VGPRs, which then hold nothing else the key loop needs, so no value
+  // is copied in and out of AGPRs. One row half (one wave per SIMD, up to
+  // 8 x 16 accumulators at D 256): AGPRs, which the matrix cores accumulate
+  // into directly, leaving the arch VGPRs to the operands (measured 8-14 %
+  // faster at D 256 and for int8 at D 128, equal for bf16 at D 128).
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if constexpr (NRH == 1)
+        asm volatile("" : "+a"(acc[db]));
+      else
+        asm volatile("" : "+v"(acc[db]));
+    }
+  };
 
   const char* kbase = reinterpret_cast<const char*>(p.k);
   const char* vbase = reinterpret_cast<const char*>(p.v);
@@ -732,8 +747,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     // more than 2^8 (rare; the wave votes first)
     const bool need = (mrun == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
     if (__any(need)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
+      pin_acc();
       const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
       const float mnew = fmaxf(mrun, mt + mu);
       const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
@@ -746,8 +760,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] -= shift;
       mrun = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
+      pin_acc();
     }
     // ---- probabilities times the V scale as the bf16 P^T operand
     bf16x8 pf[2];
@@ -805,10 +818,8 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         acc[db] = mfma(vf, pf[kh], acc[db]);
       }
     // The accumulators only meet VALU code in the rare rescale and at the
-    // end: keep them in one register assignment across blocks (arch VGPRs:
-    // with no AGPR use the whole register budget goes to them).
-#pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(acc[db]));
+    // end: keep them in one register assignment across blocks.
+    pin_acc();
   };
 
   // ---- the key loop ----------------------------------------------------------
