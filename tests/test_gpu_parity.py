@@ -147,3 +147,22 @@ def test_edge_contexts(n, ctx):
         for mode, S in (("single", 1), ("split", 8)):
             o, _, _ = run(p, mode, num_splits=S, impl=impl, ws_fill=float("nan"))
             _check(p, o, n, f"cfg{n} ctx={ctx} {mode} S={S} {impl}")
+
+
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_maximum_split_count(n):
+    """The largest uniform split count the library accepts: most splits of a
+    short request are empty (chunks are rounded up to whole tiles), and the
+    combine takes every request's records in batches (64 per lane). Scratch
+    records start NaN-filled; the same count again gives the same bits."""
+    import split_kv_flash_decode_amd as skv
+    S = skv.SKV_MAX_SPLITS
+    p = _problem(n, seed=150 + n)
+    for impl in IMPLS[n]:
+        o, _, _ = run(p, "split", num_splits=S, impl=impl, ws_fill=float("nan"))
+        _check(p, o, n, f"cfg{n} S={S} {impl}")
+        o2, _, _ = run(p, "split", num_splits=S, impl=impl, ws_fill=float("nan"))
+        assert torch.equal(o.view(torch.int16) if o.dtype != torch.float32 else o.view(torch.int32),
+                           o2.view(torch.int16) if o2.dtype != torch.float32 else o2.view(torch.int32))
+    with pytest.raises(skv.SkvError):
+        run(p, "split", num_splits=S + 1, impl=IMPLS[n][0])
