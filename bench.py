@@ -359,7 +359,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--block-size", type=int, default=0)
     ap.add_argument("--v-layout", default="")
