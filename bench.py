@@ -21,8 +21,9 @@ resident in HBM before timing starts. Prints one JSON line:
               per launch measured with rocprofv3 counters (FETCH_SIZE +
               WRITE_SIZE, scaled by a copy-kernel calibration) when a
               committed measurement for the current kernel source exists
-  cpu_baseline  the fp64 oracle timed on host cores over a bounded sample of
-              the same workload (whole requests), as effective TB/s
+  cpu_baseline  the fp64 oracle over every request of the workload, on one
+              single-threaded worker process per host core (at most 16),
+              as effective TB/s, with the single-core time and the CPU model
   copy_kernel  a 1 GiB device copy timed after the steps (bytes read plus
               written per second): what a plain streaming kernel reaches on
               this box, beside the published peak
@@ -130,37 +131,132 @@ def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> dict:
             "frac_of_peak": round(sorted(rates)[1] / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(problem, spec, budget_s: float = 12.0, max_requests: int = 200):
-    """Time the fp64 oracle on whole requests of the workload until ~budget_s."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_ONE_THREAD_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
+def _oracle_worker_init():
+    """Worker set-up: one BLAS / OpenMP thread per worker process (the
+    environment already says so; the limit is applied again once numpy's BLAS
+    is loaded)."""
+    import numpy  # noqa: F401  (loads the BLAS the limit applies to)
     import threadpoolctl
 
-    import oracle
-    from skvgen import extract_request
+    threadpoolctl.threadpool_limits(1)
+    import torch
 
-    done, t_oracle, nbytes = 0, 0.0, 0
-    for b in range(min(max_requests, spec.B)):
-        sub = extract_request(problem, b)
-        arrays = sub.host_arrays()
-        s = sub.spec
-        t = time.perf_counter()
-        oracle.decode_attention(arrays, R=s.R, Hq=s.Hq, Hkv=s.Hkv, D=s.D, causal=s.causal,
-                                window=s.window, scale=s.scale, q_dtype=s.q_dtype,
-                                kv_dtype=s.kv_dtype, paged=True, block_size=s.block_size,
-                                v_layout=s.v_layout, has_sink=s.sinks)
-        t_oracle += time.perf_counter() - t
-        nbytes += spec_bytes(sub.spec)
-        done += 1
-        if t_oracle >= budget_s:
+    torch.set_num_threads(1)
+
+
+def _worker_pid(_):
+    time.sleep(0.05)
+    return os.getpid()
+
+
+def _oracle_request(task):
+    """One request of the workload, built on this host core (seeded by request)
+    and run through the fp64 oracle; returns (worker pid, oracle seconds,
+    logical bytes). Only the oracle call is timed."""
+    import oracle
+    from skvgen import config_spec, make_problem
+
+    config, spec_over, seed, b = task
+    full = config_spec(config, **spec_over)
+    spec = full.with_(ctx=(full.ctx[b],), B=1, name=f"{full.name}_req{b}")
+    prob = make_problem(spec, seed=seed * 100003 + b, device="cpu")
+    arrays = prob.host_arrays()
+    t = time.perf_counter()
+    oracle.decode_attention(arrays, R=spec.R, Hq=spec.Hq, Hkv=spec.Hkv, D=spec.D, causal=spec.causal,
+                            window=spec.window, scale=spec.scale, q_dtype=spec.q_dtype,
+                            kv_dtype=spec.kv_dtype, paged=True, block_size=spec.block_size,
+                            v_layout=spec.v_layout, has_sink=spec.sinks)
+    dt = time.perf_counter() - t
+    return os.getpid(), dt, spec_bytes(spec)
+
+
+def start_oracle_pool():
+    """Worker processes for the CPU baseline, one per host core of this job's
+    share (at most 16), started before this process touches the GPU (fresh
+    interpreters, no GPU state inherited), each with one BLAS thread."""
+    import multiprocessing as mp
+
+    visible = len(os.sched_getaffinity(0))
+    n = max(1, min(16, visible))
+    saved = {k: os.environ.get(k) for k in _ONE_THREAD_ENV}
+    for k in _ONE_THREAD_ENV:
+        os.environ[k] = "1"
+    try:
+        pool = mp.get_context("spawn").Pool(n, initializer=_oracle_worker_init)
+        # every worker has imported its modules before the GPU timing starts, so
+        # their start-up does not compete with the timed steps for host cores
+        pids = set()
+        while len(pids) < n:
+            pids.update(pool.map(_worker_pid, range(4 * n), chunksize=1))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool, n, visible
+
+
+def cpu_baseline(pool, n_workers: int, visible: int, config: int, spec_over: dict, spec, seed: int,
+                 budget_s: float = 90.0) -> dict:
+    """The fp64 oracle over the requests of the workload, one request per task
+    on ``n_workers`` single-threaded worker processes, until every request is
+    done or ``budget_s`` of wall time has passed (the sample then says how
+    many). ``value`` is the logical bytes of the requests done over the
+    makespan of their oracle calls (the largest sum of oracle seconds any one
+    worker spent); ``single_core_s`` is the sum over them (one core)."""
+    t0 = time.perf_counter()
+    res = []
+    tasks = [(config, spec_over, seed, b) for b in range(spec.B)]
+    for r in pool.imap_unordered(_oracle_request, tasks, chunksize=1):
+        res.append(r)
+        if len(res) % 16 == 0 or len(res) == spec.B:
+            print(f"[bench] oracle: {len(res)} of {spec.B} requests, {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
+        if time.perf_counter() - t0 > budget_s and len(res) < spec.B:
+            pool.terminate()
             break
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    wall = time.perf_counter() - t0
+    per_worker = {}
+    nbytes = 0
+    for pid, dt, nb in res:
+        per_worker[pid] = per_worker.get(pid, 0.0) + dt
+        nbytes += nb
+    makespan = max(per_worker.values())
+    single = sum(dt for _, dt, _ in res)
+    done = len(res)
+    which = f"all {spec.B} requests" if done == spec.B else f"{done} of {spec.B} requests (wall-time cap)"
     return {
-        "value": round(nbytes / t_oracle / 1e12, 6),
+        "value": round(nbytes / makespan / 1e12, 6),
         "unit": "TB/s",
-        "cores": int(cores),
+        "cores": n_workers,
         "kind": "oracle",
-        "sample": f"{done} of {spec.B} requests (whole requests, {nbytes} logical bytes) in "
-                  f"{t_oracle:.2f} s; {t_oracle / done * spec.B * 1e6:.0f} us/step extrapolated",
+        "sample": (f"{which} of the workload, each built on the host (seeded per request) and run "
+                   f"through the fp64 oracle once, on {n_workers} worker processes with one BLAS "
+                   f"thread each; value = {nbytes} logical bytes / {makespan:.2f} s (largest per-worker "
+                   f"oracle time)"),
+        "us_per_step": round(makespan * 1e6 * spec.B / done, 1),
+        "single_core_s": round(single, 3),
+        "single_core_s_per_step": round(single * spec.B / done, 3),
+        "wall_s_incl_input_build": round(wall, 2),
+        "requests_done": done,
+        "workers_used": len(per_worker),
+        "host_cpus_visible": visible,
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -179,10 +275,10 @@ PAGE_TABLE = [
 
 
 def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f32",
-                mode: str = "two_stage", event_free_pass: bool = False):
-    """Generate the workload, run the planned step (host plan refresh, metadata
-    copy, partial, combine) ``warmup`` + ``steps`` times; returns
-    (ms per step, partial ms list, combine ms list, plan, problem).
+                mode: str = "two_stage", event_free_pass: bool = False, excl_plan_pass: bool = False,
+                problem=None) -> dict:
+    """Generate the workload (or take ``problem``), run the planned step (host
+    plan refresh, metadata copy, partial, combine) ``warmup`` + ``steps`` times.
 
     ``mode`` "fused": the single-kernel split + merge instead of partial +
     combine (its time is reported as the partial time, combine 0);
@@ -197,15 +293,17 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     write has pushed the inputs out of L2 and the 256 MB last-level cache
     (``cold_ms``, the median): the cache-cold time of workloads small enough
     to stay cache-resident between back-to-back steps.
-    Returns (ms per step, partial ms list, combine ms list, plan, problem,
-    cold ms or None)."""
+    ``excl_plan_pass``: one more pass of ``steps`` steps with the plan left as
+    it is (lengths unchanged): partial + combine only (``ms_excl_plan``).
+    Returns a dict: ms (per step), part_ms, comb_ms (lists), plan, problem,
+    cold_ms, ms_excl_plan (None when not measured)."""
     import torch
 
     import split_kv_flash_decode_amd as skv
     from skvgen import make_problem
 
     dev = torch.device("cuda:0")
-    p = make_problem(spec, seed=seed, device=dev)
+    p = problem if problem is not None else make_problem(spec, seed=seed, device=dev)
     torch.cuda.synchronize()
     o = torch.empty_like(p.q)
     d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
@@ -220,11 +318,12 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     stream = torch.cuda.current_stream()
     counters = torch.zeros(spec.B * spec.Hkv, dtype=torch.int32, device=dev)
 
-    def step(ev=None):
-        if mode == "device_plan":
-            plan.refresh_device(p.ctx)
-        else:
-            plan.refresh(host_ctx)
+    def step(ev=None, refresh=True):
+        if refresh:
+            if mode == "device_plan":
+                plan.refresh_device(p.ctx)
+            else:
+                plan.refresh(host_ctx)
         if ev is not None:
             ev[0].record(stream)
         if mode == "fused":
@@ -262,6 +361,14 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
         step(e)
     torch.cuda.synchronize()
     comb_ms = [e[1].elapsed_time(e[2]) for e in extra]
+    excl_ms = None
+    if excl_plan_pass:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(refresh=False)
+        torch.cuda.synchronize()
+        excl_ms = (time.perf_counter() - t0) * 1e3 / steps
     cold_ms = None
     if event_free_pass:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -276,7 +383,9 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
             times.append(e0.elapsed_time(e1))
         cold_ms = sorted(times)[len(times) // 2]
         del flush
-    return (plain_ms if event_free_pass else wall * 1e3 / steps), part_ms, comb_ms, plan, p, cold_ms
+    return {"ms": plain_ms if event_free_pass else wall * 1e3 / steps, "part_ms": part_ms,
+            "comb_ms": comb_ms, "plan": plan, "problem": p, "cold_ms": cold_ms, "ms_excl_plan": excl_ms,
+            "output": o}
 
 
 def table(args) -> int:
@@ -288,7 +397,8 @@ def table(args) -> int:
         spec = config_spec(n, block_size=bs, v_layout=vl, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p, cold_ms = timed_steps(spec, n, steps, warmup, event_free_pass=True)
+        r = timed_steps(spec, n, steps, warmup, event_free_pass=True)
+        ms, part_ms, comb_ms, plan, p, cold_ms = r["ms"], r["part_ms"], r["comb_ms"], r["plan"], r["problem"], r["cold_ms"]
         tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
         print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
                           "effective_TBps": round(tbs, 3),
@@ -331,8 +441,8 @@ def next_rows(args) -> int:
         spec = config_spec(n, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        ms, part_ms, comb_ms, plan, p, cold_ms = timed_steps(spec, n, steps, warmup, record_dtype=rec,
-                                                             mode=mode, event_free_pass=True)
+        r = timed_steps(spec, n, steps, warmup, record_dtype=rec, mode=mode, event_free_pass=True)
+        ms, part_ms, comb_ms, plan, p, cold_ms = r["ms"], r["part_ms"], r["comb_ms"], r["plan"], r["problem"], r["cold_ms"]
         part_us = sum(part_ms) / len(part_ms) * 1e3
         unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
         alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
@@ -355,6 +465,98 @@ def next_rows(args) -> int:
     return 0
 
 
+def timed_uniform(spec, S: int, seed: int, steps: int, warmup: int, problem=None) -> dict:
+    """The uniform-split call (skv_attention_decode_paged_splitkv with S
+    splits: partial + combine, no plan) timed like ``timed_steps``: a pass
+    without events (warm), then each call alone after a 1 GiB write (cold)."""
+    import torch
+
+    import split_kv_flash_decode_amd as skv
+    from skvgen import make_problem
+
+    dev = torch.device("cuda:0")
+    p = problem if problem is not None else make_problem(spec, seed=seed, device=dev)
+    o = torch.empty_like(p.q)
+    d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
+                      window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
+    a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
+                      page_table=p.page_table, sinks=p.sinks)
+    ws = skv.Workspace(d, skv.uniform_slots(d, S), dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        skv.attention_decode_paged_splitkv(d, a, S, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    warm = (time.perf_counter() - t0) * 1e3 / steps
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    times = []
+    for k in range(min(steps, 50)):
+        flush.fill_(float(k))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    return {"ms": warm, "cold_ms": sorted(times)[len(times) // 2], "problem": p}
+
+
+def all_configs(args) -> int:
+    """One JSON line per (workload, split mode): the five workloads with the
+    planner step, plus the uniform split counts the single-request and the
+    verifier workloads name. Warm: back-to-back steps without events; cold:
+    each step alone after a 1 GiB write; excl_plan: partial + combine only."""
+    import torch
+
+    from skvgen import config_spec
+
+    for n in (1, 2, 3, 4, 5):
+        spec = config_spec(n)
+        small = max(spec.ctx) * spec.B < 10_000_000
+        steps, warmup = (400, 50) if small else (args.steps, args.warmup)
+        nbytes = spec_bytes(spec)
+        unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
+        alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
+        r = timed_steps(spec, n, steps, warmup, event_free_pass=True, excl_plan_pass=True)
+        part_us = sum(r["part_ms"]) / len(r["part_ms"]) * 1e3
+        row = {"config": n, "workload": workload_name(spec), "mode": "planner",
+               "plan_items": r["plan"].info.num_items, "logical_bytes": nbytes,
+               "us_per_step_warm": round(r["ms"] * 1e3, 2),
+               "us_per_step_cold": round(r["cold_ms"] * 1e3, 2),
+               "us_per_step_excl_plan": round(r["ms_excl_plan"] * 1e3, 2),
+               "TBps_warm": round(nbytes / (r["ms"] * 1e-3) / 1e12, 4),
+               "TBps_cold": round(nbytes / (r["cold_ms"] * 1e-3) / 1e12, 4),
+               "frac_warm": round(nbytes / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "frac_cold": round(nbytes / (r["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "partial_us_mean": round(part_us, 2),
+               "combine_us_mean": round(sum(r["comb_ms"]) / len(r["comb_ms"]) * 1e3, 2),
+               "partial_roofline_frac": round(alg / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+               "steps": steps, "warmup": warmup}
+        print(json.dumps(row), flush=True)
+        p = r["problem"]
+        for S in (spec.splits or ()):
+            u = timed_uniform(spec, S, n, steps, warmup, problem=p)
+            print(json.dumps({"config": n, "workload": workload_name(spec), "mode": f"uniform S={S}",
+                              "us_per_step_warm": round(u["ms"] * 1e3, 2),
+                              "us_per_step_cold": round(u["cold_ms"] * 1e3, 2),
+                              "TBps_warm": round(nbytes / (u["ms"] * 1e-3) / 1e12, 4),
+                              "TBps_cold": round(nbytes / (u["cold_ms"] * 1e-3) / 1e12, 4),
+                              "frac_warm": round(nbytes / (u["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "frac_cold": round(nbytes / (u["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "steps": steps, "warmup": warmup}), flush=True)
+        del r, p
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,7 +567,6 @@ def main(argv=None) -> int:
     ap.add_argument("--v-layout", default="")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 1 GiB device-to-device copies (counter calibration)")
     ap.add_argument("--table", action="store_true",
@@ -374,6 +575,9 @@ def main(argv=None) -> int:
     ap.add_argument("--next", action="store_true",
                     help="time the adjacent variants (fp16 Q/O, bf16 records, fused call, device "
                          "plan refresh, verify masks) against the default call on the same workloads")
+    ap.add_argument("--all", action="store_true",
+                    help="per-workload table: the five workloads (planner step) and the uniform split "
+                         "counts they name, warm / cache-cold / plan-excluded time per step")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -381,6 +585,12 @@ def main(argv=None) -> int:
               "(the path needs no collectives: requests and KV heads shard without exchange)",
               file=sys.stderr)
         return 2
+
+    side_mode = args.calibrate_copy or args.next or args.table or args.all
+    pool = None
+    if not side_mode and not args.no_cpu_baseline:
+        # the oracle's worker processes start before anything touches the GPU
+        pool, n_workers, visible = start_oracle_pool()
 
     import torch
 
@@ -402,6 +612,8 @@ def main(argv=None) -> int:
         return next_rows(args)
     if args.table:
         return table(args)
+    if args.all:
+        return all_configs(args)
     overrides = {}
     if args.block_size:
         overrides["block_size"] = args.block_size
@@ -410,8 +622,11 @@ def main(argv=None) -> int:
     spec = config_spec(args.config, **overrides)
     print(f"[bench] generating {spec.name} on cuda:0 and timing ...", file=sys.stderr, flush=True)
     t = time.time()
-    ms_per_step, part_ms, comb_ms, plan, p, _ = timed_steps(spec, args.seed, args.steps, args.warmup)
+    r = timed_steps(spec, args.seed, args.steps, args.warmup, excl_plan_pass=True)
+    ms_per_step, part_ms, comb_ms, plan = r["ms"], r["part_ms"], r["comb_ms"], r["plan"]
+    ms_excl_plan = r["ms_excl_plan"]
     print(f"[bench] done in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
+    del r
     nbytes = spec_bytes(spec)
     tbs = nbytes / (ms_per_step * 1e-3) / 1e12
 
@@ -422,6 +637,7 @@ def main(argv=None) -> int:
     achieved = alg_bytes / (part_mean * 1e-3) / 1e9
     key = f"cfg{args.config}_bs{spec.block_size}_{spec.v_layout}"
     traffic = measured_traffic(key)
+    fp8_scores = spec.kv_dtype == "fp8" and spec.q_dtype == "bf16"
 
     result = {
         "metric": "decode-attention us/step + effective KV TB/s (fraction of HBM peak)",
@@ -432,12 +648,17 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_excl_plan": round(ms_excl_plan * 1e3, 2),
         "hbm_fraction": round(tbs * 1e3 / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tbs / 4.607, 4) if (args.config == 4 and spec.block_size == 16
                                                  and spec.v_layout == "plain") else None,
-        "dtype": "bf16",
+        "dtype": "fp8+bf16" if fp8_scores else spec.q_dtype,
+        "dtype_detail": ("scores Q.K^T on the fp8 matrix cores (e4m3 K codes, bf16 Q split into two "
+                         "e4m3 parts with power-of-two block scales), P.V on the bf16 matrix cores, "
+                         "softmax and accumulation in fp32, bf16 output"
+                         if fp8_scores else f"{spec.q_dtype} Q/O, {spec.kv_dtype} KV, fp32 accumulation"),
         "data": "synthetic",
         "config": {
             "workload": workload_name(spec),
@@ -449,6 +670,9 @@ def main(argv=None) -> int:
             "plan_capacity": plan.capacity,
             "partial_us_mean": round(part_mean * 1e3, 2),
             "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
+            "timing": ("value and ms_per_step: wall clock over the timed steps, each a host plan "
+                       "refresh + metadata copy + partial + combine; us_per_step_excl_plan: the same "
+                       "number of steps with the plan left unchanged (partial + combine only)"),
         },
         "roofline": {
             "bound": "hbm",
@@ -461,9 +685,14 @@ def main(argv=None) -> int:
         "cpu_baseline": None,
     }
     result["copy_kernel"] = copy_bandwidth()
-    if not args.no_cpu_baseline:
+    if pool is not None:
         print("[bench] timing the fp64 oracle on host cores ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(p, spec, budget_s=args.cpu_budget)
+        try:
+            result["cpu_baseline"] = cpu_baseline(pool, n_workers, visible, args.config, overrides, spec,
+                                                  args.seed)
+        finally:
+            pool.close()
+            pool.join()
     print(json.dumps(result), flush=True)
     return 0
 

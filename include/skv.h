@@ -104,8 +104,12 @@
  * acc is stored as fp32, or as bf16 (round to nearest even) when the
  * descriptor's record_dtype is SKV_BF16: half the record bytes, the layout of
  * the planned-reduction page ([PA] Changes: bf16 partial output plus two fp32
- * per row; here the un-normalised acc with m and l, which carries the same
- * information).
+ * per row; here the un-normalised acc with m and l). bf16 records are an
+ * option, not the default: their rounding moves an output element by up to
+ * 2^-8 * sum_t p_t |v_t| / sum_t p_t, so where values of opposite sign in
+ * different splits cancel, the result can exceed atol = rtol = 5e-3 against
+ * the exact merge (measured: |d| 0.021 at |O| 0.03 with queries scaled by 8).
+ * fp32 records (the default) carry no such term.
  * An empty T_s gives m = -inf, l = 0, acc = 0. Record slot numbers:
  *   uniform splits:  slot = ((b * S) + s) * Hkv + g
  *   planned splits:  slot = (req_slot0[b] + s) * Hkv + g
@@ -129,7 +133,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 3
+#define SKV_ABI_VERSION 4
 #define SKV_SPLIT_ALIGN 64    /* split boundaries are multiples of this many tokens */
 #define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
@@ -237,6 +241,11 @@ int skv_validate(const skv_desc* d, int32_t paged, int32_t num_splits, const skv
 int skv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t* l_bytes,
                        size_t* acc_bytes);
 
+/* The same sizes under the split-KV name ([DR] Design: preallocated partial
+ * buffers sized by the caller): identical to skv_workspace_size. */
+int skv_splitkv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t* l_bytes,
+                               size_t* acc_bytes);
+
 /* Records needed by a uniform split call: B * num_splits * Hkv. */
 int64_t skv_uniform_slots(const skv_desc* d, int32_t num_splits);
 
@@ -319,6 +328,31 @@ int skv_plan_capacity(const skv_plan_hints* h, const int32_t* host_ctx, int32_t*
  * int32 for capacity C from host context lengths. info may be NULL. */
 int skv_plan_fill(const skv_plan_hints* h, const int32_t* host_ctx, int32_t capacity_items,
                   int32_t* meta, int64_t meta_len, skv_plan_info* info);
+
+/* A plan as one caller-owned object ([PA] intro, Changes: the plan is made
+ * once with a fixed capacity and refreshed per call from host-known lengths).
+ * skv_plan_make copies the hints, fixes capacity_items and sets meta_len; the
+ * caller then points `meta` at a host buffer of meta_len int32 (pinned memory
+ * when it is copied to the device asynchronously) that it owns.
+ * skv_plan_refresh fills that buffer and `info` from host context lengths,
+ * keeping capacity_items. Host-only; no HIP call. */
+typedef struct skv_plan {
+  skv_plan_hints hints;      /* copied by skv_plan_make */
+  int32_t capacity_items;    /* C, fixed by skv_plan_make */
+  int64_t meta_len;          /* int32 entries the metadata block needs */
+  int32_t* meta;             /* caller-owned host buffer of meta_len int32 */
+  skv_plan_info info;        /* counts of the last refresh */
+} skv_plan;
+
+/* Make a plan. Capacity: plan->capacity_items when the caller set it > 0 on
+ * entry (e.g. from skv_plan_capacity with the host lengths), else sized from
+ * the work hint hints->total_context_length (SKV_ERR_PLAN with neither).
+ * Sets hints, capacity_items and meta_len, zeroes info; meta is untouched. */
+int skv_plan_make(const skv_plan_hints* h, skv_plan* plan);
+
+/* Refresh a made plan from host context lengths (plan->meta must be set):
+ * skv_plan_fill with the plan's hints and capacity. */
+int skv_plan_refresh(skv_plan* plan, const int32_t* host_ctx);
 
 /* Device-side refresh ([PA] intro, Changes; graph replay with changing
  * lengths): fill the DEVICE metadata block `meta_dev` (meta_len int32, for

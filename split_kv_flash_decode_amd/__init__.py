@@ -71,12 +71,21 @@ class PlanInfo(ctypes.Structure):
                 ("min_partitions", _c_i32), ("slots", ctypes.c_int64)]
 
 
+class SkvPlan(ctypes.Structure):
+    _fields_ = [("hints", PlanHints), ("capacity_items", _c_i32), ("meta_len", ctypes.c_int64),
+                ("meta", ctypes.POINTER(_c_i32)), ("info", PlanInfo)]
+
+
 EXPORTS = {
     "skv_abi_version": (_c_i32, []),
     "skv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "skv_validate": (ctypes.c_int, [ctypes.POINTER(Desc), _c_i32, _c_i32, ctypes.POINTER(Partials)]),
     "skv_workspace_size": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t),
                                           ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "skv_splitkv_workspace_size": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int64,
+                                                  ctypes.POINTER(ctypes.c_size_t),
+                                                  ctypes.POINTER(ctypes.c_size_t),
+                                                  ctypes.POINTER(ctypes.c_size_t)]),
     "skv_uniform_slots": (ctypes.c_int64, [ctypes.POINTER(Desc), _c_i32]),
     "skv_attention_decode": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_ptr]),
     "skv_attention_decode_paged": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_ptr]),
@@ -89,6 +98,8 @@ EXPORTS = {
                                          ctypes.POINTER(_c_i32)]),
     "skv_plan_fill": (ctypes.c_int, [ctypes.POINTER(PlanHints), ctypes.POINTER(_c_i32), _c_i32,
                                      ctypes.POINTER(_c_i32), ctypes.c_int64, ctypes.POINTER(PlanInfo)]),
+    "skv_plan_make": (ctypes.c_int, [ctypes.POINTER(PlanHints), ctypes.POINTER(SkvPlan)]),
+    "skv_plan_refresh": (ctypes.c_int, [ctypes.POINTER(SkvPlan), ctypes.POINTER(_c_i32)]),
     "skv_attention_decode_paged_planned": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args),
                                                           _c_ptr, _c_i32, ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_partial": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_i32,
@@ -268,6 +279,13 @@ def workspace_size(desc: Desc, slots: int):
     return m.value, l.value, a.value
 
 
+def splitkv_workspace_size(desc: Desc, slots: int):
+    m, l, a = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().skv_splitkv_workspace_size(ctypes.byref(desc), int(slots), ctypes.byref(m), ctypes.byref(l),
+                                            ctypes.byref(a)), "skv_splitkv_workspace_size")
+    return m.value, l.value, a.value
+
+
 def uniform_slots(desc: Desc, num_splits: int) -> int:
     return lib().skv_uniform_slots(ctypes.byref(desc), int(num_splits))
 
@@ -380,6 +398,25 @@ def plan_fill(hints: PlanHints, host_ctx, capacity: int, meta: torch.Tensor) -> 
                                ctypes.cast(meta.data_ptr(), ctypes.POINTER(_c_i32)), meta.numel(),
                                ctypes.byref(info)), "skv_plan_fill")
     return info
+
+
+def plan_make(hints: PlanHints, capacity: int = 0) -> SkvPlan:
+    """skv_plan_make: a plan object with fixed capacity (``capacity`` > 0, or
+    sized from ``hints.total_context_length``); its ``meta`` is still unset."""
+    plan = SkvPlan()
+    plan.capacity_items = int(capacity)
+    _check(lib().skv_plan_make(ctypes.byref(hints), ctypes.byref(plan)), "skv_plan_make")
+    return plan
+
+
+def plan_refresh(plan: SkvPlan, host_ctx, meta: torch.Tensor) -> PlanInfo:
+    """skv_plan_refresh into the host int32 tensor ``meta`` (CPU, contiguous,
+    at least ``plan.meta_len`` entries)."""
+    _need(meta.device.type == "cpu" and meta.dtype == torch.int32 and meta.is_contiguous()
+          and meta.numel() >= plan.meta_len, "meta must be a contiguous CPU int32 tensor of meta_len entries")
+    plan.meta = ctypes.cast(meta.data_ptr(), ctypes.POINTER(_c_i32))
+    _check(lib().skv_plan_refresh(ctypes.byref(plan), _ctx_array(host_ctx)), "skv_plan_refresh")
+    return plan.info
 
 
 def plan_refresh_device(hints: PlanHints, ctx_dev: torch.Tensor, capacity: int, meta_dev: torch.Tensor,

@@ -1,8 +1,8 @@
 // Combine kernel: merge the partial records of every split of a request into
-// the output ("combine kernel ... merged by the flash-decoding formula",
-// tiny-llm #11 split-KV design record, "Design"; the reducer iterates only
-// each request's actual partitions, aiter #5628 "tune MTP work budgets and
-// planned reduction", Changes).
+// the output with the flash-decoding merge (tiny-llm #11 split-KV design
+// record, "Design": a second kernel does the merge); the reducer visits only
+// the partitions a request actually has (aiter #5628 "tune MTP work budgets
+// and planned reduction", Changes).
 //
 // One 256-thread workgroup per (request, KV head, chunk of rows); four
 // adjacent threads share one output (four consecutive d of one query row)

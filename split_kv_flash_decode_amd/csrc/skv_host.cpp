@@ -282,6 +282,11 @@ int skv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t
   return SKV_OK;
 }
 
+int skv_splitkv_workspace_size(const skv_desc* d, int64_t slots, size_t* m_bytes, size_t* l_bytes,
+                               size_t* acc_bytes) {
+  return skv_workspace_size(d, slots, m_bytes, l_bytes, acc_bytes);
+}
+
 int64_t skv_uniform_slots(const skv_desc* d, int32_t num_splits) {
   if (!d || num_splits < 1) return 0;
   return (int64_t)d->batch * num_splits * d->num_kv_heads;
@@ -424,6 +429,29 @@ int skv_plan_fill(const skv_plan_hints* h, const int32_t* host_ctx, int32_t capa
     info->slots = (int64_t)capacity_items * r.Hkv;
   }
   return SKV_OK;
+}
+
+int skv_plan_make(const skv_plan_hints* h, skv_plan* plan) {
+  int rc = check_hints(h);
+  if (rc) return rc;
+  if (!plan) return SKV_ERR_NULL;
+  int32_t cap = plan->capacity_items;
+  if (cap <= 0) {
+    if (h->total_context_length <= 0) return SKV_ERR_PLAN;
+    rc = skv_plan_capacity(h, nullptr, &cap);
+    if (rc) return rc;
+  }
+  if (cap < h->batch) return SKV_ERR_CAPACITY;
+  plan->hints = *h;
+  plan->capacity_items = cap;
+  plan->meta_len = skv_plan_meta_len(h->batch, cap);
+  memset(&plan->info, 0, sizeof(plan->info));
+  return SKV_OK;
+}
+
+int skv_plan_refresh(skv_plan* plan, const int32_t* host_ctx) {
+  if (!plan) return SKV_ERR_NULL;
+  return skv_plan_fill(&plan->hints, host_ctx, plan->capacity_items, plan->meta, plan->meta_len, &plan->info);
 }
 
 int skv_attention_decode_paged_planned(const skv_desc* d, const skv_args* a,

@@ -143,6 +143,15 @@ SKV_HD void row_range(int ctx, int R, int causal, int window, int j, int* vlo, i
   *vhi = hi;
 }
 
+// The matrix-core kernel addresses a transposed-V row of a contiguous cache
+// with a 32-bit per-lane byte offset from the (request, KV head) base:
+// (D - 1) * kv_capacity * bytes + 16 must stay below 2^31, else the call goes
+// to the vector kernel (64-bit addressing throughout).
+SKV_HD bool mfma_offsets_fit(int paged, int v_layout, int D, int kv_cap, int kv_bytes) {
+  if (paged || v_layout != SKV_V_TRANSPOSED) return true;
+  return (long long)D * kv_cap * kv_bytes < (1ll << 31);
+}
+
 // Work item -> (request, split, splits of the request, record item index).
 struct Item {
   int b, s, S, slot_item;

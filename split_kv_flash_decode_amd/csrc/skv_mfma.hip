@@ -1026,7 +1026,8 @@ bool mfma_supported(const Params& p) {
   // per-wave LDS ring, so that shape stays on the vector kernel
   if (p.D == 256 && p.kv_dtype == SKV_BF16) return false;
   if (p.paged) return p.block_size >= 16;
-  return p.kv_cap % 16 == 0;
+  const int eb = p.kv_dtype == SKV_BF16 ? 2 : 1;
+  return p.kv_cap % 16 == 0 && mfma_offsets_fit(0, p.v_layout, p.D, p.kv_cap, eb);
 }
 
 int launch_partial_mfma(Params p, void* stream) {

@@ -2,11 +2,13 @@
 // included) and the one used for few query rows per KV head.
 //
 // One wave (64 lanes) per (work item, KV head, chunk of up to 8 query rows).
-// A work item is one split of one request ("partial kernel: grid = (Hq,
-// num_splits), each block computes its own logical range from the device
-// visible_tokens with chunk = ceil(visible / splits) and emits a local
-// (m_i, l_i, acc_i)", tiny-llm #11 split-KV design record, "Design"), or the
-// whole request in single-pass mode, where the record is finalized in place.
+// A work item is one split of one request, or the whole request in
+// single-pass mode, where the record is finalized in place. The design record
+// of tiny-llm #11 ("split-KV decode attention design record", section
+// "Design") lays the partial kernel out over (head, split): each split finds
+// its own key range from the visible length held on the device, with a chunk
+// length of the visible keys divided by the split count, rounded up, and
+// writes its own running maximum, sum and weighted values.
 //
 // Per 64-key tile: lane t owns key t for Q.K^T (its K row is read with
 // 16-byte loads and dequantized in registers, Q comes from LDS as broadcasts);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), f"{n} missing from libskv.so"
     assert set(names) == set(skv.EXPORTS), "binding and header disagree"
-    assert skv.abi_version() == 3
+    assert skv.abi_version() == 4
 
 
 def _desc(**kw):
@@ -277,3 +277,100 @@ def test_planner_budget_counts_workgroups_per_head():
     assert info.num_items == 3200 and info.max_partitions == 16 and cap == 3200
     with pytest.raises(skv.SkvError):
         _plan([100], workgroups_per_head=-1)
+
+
+# ---------------------------------------------------------------------------
+# the boundary's names against the contract that lists them
+
+# Every export the split-KV contract names, and the call that provides it here.
+# Where the shipped name differs, the mapping says how (the documented reading).
+CONTRACT = {
+    "skv_attention_decode": "skv_attention_decode",
+    "skv_attention_decode_paged": "skv_attention_decode_paged",
+    "skv_attention_decode_splitkv": "skv_attention_decode_splitkv",
+    "skv_attention_decode_paged_splitkv": "skv_attention_decode_paged_splitkv",
+    "skv_splitkv_workspace_size": "skv_splitkv_workspace_size",   # also as skv_workspace_size
+    "skv_plan_make": "skv_plan_make",                             # capacity/fill are its parts
+    "skv_plan_refresh": "skv_plan_refresh",
+    "skv_validate": "skv_validate",                               # with an added `paged` argument
+    "skv_status_str": "skv_status_str",
+    "skv_abi_version": "skv_abi_version",
+}
+
+
+def test_contract_names_are_exported():
+    L = _lib()
+    for want, have in CONTRACT.items():
+        assert hasattr(L, have), f"{want} -> {have} missing"
+
+
+def test_splitkv_workspace_size_is_workspace_size():
+    for kw in (dict(), dict(B=3, R=16, Hq=24, Hkv=4, D=256), dict(record_dtype="bf16")):
+        d = _desc(**kw)
+        for slots in (0, 1, 3200):
+            assert skv.splitkv_workspace_size(d, slots) == skv.workspace_size(d, slots)
+
+
+def test_plan_make_and_refresh_equal_capacity_and_fill():
+    _lib()
+    for ctx, kw in (([200000] * 200, dict()), ([200000] + [1024] * 15, dict(window=4096)),
+                    ([20676], dict(ctas_per_cu=1, workgroups_per_head=3))):
+        R = 16 if len(ctx) == 1 else 4
+        h = skv.plan_hints(len(ctx), R, 4 if len(ctx) == 1 else 1, **kw)
+        cap = skv.plan_capacity(h, ctx)
+        meta_ref = torch.zeros(skv.plan_meta_len(len(ctx), cap), dtype=torch.int32)
+        info_ref = skv.plan_fill(h, ctx, cap, meta_ref)
+        plan = skv.plan_make(h, cap)                      # explicit capacity
+        assert plan.capacity_items == cap and plan.meta_len == meta_ref.numel()
+        meta = torch.full((plan.meta_len,), -7, dtype=torch.int32)
+        info = skv.plan_refresh(plan, ctx, meta)
+        assert torch.equal(meta, meta_ref)
+        assert (info.num_items, info.capacity_items, info.max_partitions, info.slots) == \
+            (info_ref.num_items, info_ref.capacity_items, info_ref.max_partitions, info_ref.slots)
+        # refresh with other lengths keeps the capacity
+        info2 = skv.plan_refresh(plan, [max(1, c // 3) for c in ctx], meta)
+        assert info2.capacity_items == cap and int(meta[1]) == cap
+    # capacity from the work hint alone: B200 x 200k (total 40M keys) -> 3200
+    h = skv.plan_hints(200, 4, 1, total_context_length=200 * 200000)
+    assert skv.plan_make(h).capacity_items == 3200
+    with pytest.raises(skv.SkvError):
+        skv.plan_make(skv.plan_hints(4, 4, 1))            # neither a capacity nor a work hint
+    plan = skv.plan_make(skv.plan_hints(4, 4, 1), 8)
+    assert skv.lib().skv_plan_refresh(ctypes.byref(plan), None) == -1   # no lengths
+    assert skv.lib().skv_plan_refresh(None, None) == -1
+
+
+def test_validate_takes_paged_or_contiguous():
+    """skv_validate(d, paged, num_splits, p): the contract's three-argument form
+    plus `paged`, since a descriptor carries both layouts' fields and only the
+    caller knows which entry point it will call."""
+    d = _desc()
+    d.kv_capacity = 0                                     # fine for a paged call
+    assert skv.validate(d, True, 0) == 0
+    assert skv.validate(d, False, 0) == -2                # a contiguous call needs kv_capacity
+    d.kv_capacity = 4096
+    d.max_pages = 0
+    assert skv.validate(d, False, 0) == 0
+    assert skv.validate(d, True, 0) == -2
+
+
+def test_matrix_core_kernel_refuses_32_bit_offset_overflow():
+    """Contiguous transposed V: the matrix-core kernel's per-lane byte offset
+    (D - 1) * kv_capacity * bytes must fit in 31 bits; larger caches go to the
+    vector kernel (auto) or are refused (explicit matrix-core)."""
+    _lib()
+    q = torch.zeros(1, 4, 16, 256, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 16, 256, dtype=torch.uint8)
+
+    def desc(cap, impl, vl="transposed"):
+        d = skv.make_desc(q, k, k.clone().view(1, 1, 256, 16) if vl == "transposed" else k.clone(),
+                          paged=False, causal=True, impl=impl, v_layout=vl)
+        d.kv_capacity = cap
+        return d
+
+    fits = (1 << 31) // 256 - 16                          # 8,388,592 keys: 256 * cap < 2^31
+    assert skv.validate(desc(fits, "mfma"), False, 0) == 0
+    too_big = (1 << 31) // 256                            # 256 * cap == 2^31
+    assert skv.validate(desc(too_big, "mfma"), False, 0) == -6
+    assert skv.validate(desc(too_big, "auto"), False, 0) == 0
+    assert skv.validate(desc(too_big, "mfma", "plain"), False, 0) == 0   # plain V: 64-bit rows

@@ -13,12 +13,16 @@ partial wrote shows up as NaN. The uniform split counts the workloads name
 output, both kernel families. So do the adjacent variants ``bench.py --next``
 times (fp16 Q/O, bf16 records, verify masks, the device plan refresh), in
 that same step, on the same samples; bf16 records add the bound of their own
-rounding (2^-8 times the oracle's output on |V|).
+rounding (2^-8 times the oracle's output on |V|). The other three B200 rows
+of the planned-reduction page's Performance table (page 128, transposed V)
+and the mixed batch with a 4096-key window and sinks run here as well.
 """
 
 from __future__ import annotations
 
 import gc
+import json
+import os
 
 import pytest
 import torch
@@ -30,6 +34,16 @@ from tests.helpers import compare, oracle_abs_value_output, oracle_output
 pytestmark = pytest.mark.gpu
 
 SAMPLES = {2: None, 3: None, 4: (0, 97, 199), 5: (0, 1, 15)}
+
+
+def _record(name, b, ctx, st):
+    """Append one request's error statistics to $SKV_ACCURACY_OUT (JSON lines),
+    when that variable names a file: the per-workload accuracy summary."""
+    path = os.environ.get("SKV_ACCURACY_OUT")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps({"workload": name, "request": int(b), "ctx": int(ctx), **st}) + "\n")
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5])
@@ -46,6 +60,7 @@ def test_full_size_bench_step_matches_oracle(n):
             ref = oracle_output(sub)[0]
             st = compare(out[b], ref, "lowp")
             print(f"[full cfg{n} request {b} ctx {spec.ctx[b]}] {st}", flush=True)
+            _record(f"cfg{n}", b, spec.ctx[b], st)
             assert st["ok"], (n, b, st)
     finally:
         del p, o, ws, plan
@@ -66,10 +81,21 @@ def test_full_size_uniform_split_counts(n, S):
         o, _, _ = run(p, "split", num_splits=S, impl=impl, ws_fill=float("nan"))
         st = compare(to_f64(o), ref, "f32" if spec.kv_dtype == "f32" else "lowp")
         print(f"[full cfg{n} S={S} {impl}] {st}", flush=True)
+        _record(f"cfg{n}_S{S}_{impl}", 0, spec.ctx[0], st)
         assert st["ok"], (n, S, impl, st)
 
 
 VARIANTS = [
+    # the other three B200 rows of the planned-reduction page's Performance table
+    ("cfg4_bs128_plain", 4, {"block_size": 128}, "f32", False),
+    ("cfg4_bs16_transposed", 4, {"v_layout": "transposed"}, "f32", False),
+    ("cfg4_bs128_transposed", 4, {"block_size": 128, "v_layout": "transposed"}, "f32", False),
+    # the mixed batch with the 4096-key sliding window and per-head sinks
+    ("cfg5_window4096_sinks", 5, {"window": 4096, "sinks": True}, "f32", False),
+    # sharp queries (Q x 8, |O| ~ 1): where the 5e-3 relative bound bites at full size
+    ("cfg4_sharp", 4, {"q_mult": 8.0}, "f32", False),
+    ("cfg3_sharp", 3, {"q_mult": 8.0}, "f32", False),
+    ("cfg5_sharp_window4096_sinks", 5, {"q_mult": 8.0, "window": 4096, "sinks": True}, "f32", False),
     ("cfg4_f16", 4, {"q_dtype": "f16"}, "f32", False),
     ("cfg4_bf16_records", 4, {}, "bf16", False),
     ("cfg4_tree_mask", 4, {"verify": "tree"}, "f32", False),
@@ -95,6 +121,7 @@ def test_full_size_variant_rows_match_oracle(name, n, over, rec, dev_plan):
             extra = 2.0 ** -8 * oracle_abs_value_output(sub)[0] if rec == "bf16" else None
             st = compare(out[b], oracle_output(sub)[0], "lowp", extra=extra)
             print(f"[full {name} request {b} ctx {spec.ctx[b]}] {st}", flush=True)
+            _record(name, b, spec.ctx[b], st)
             assert st["ok"], (name, b, st)
     finally:
         del p, o, ws, plan
