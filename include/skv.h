@@ -156,6 +156,12 @@ extern "C" {
 #define SKV_ERR_LAUNCH (-7)        /* the HIP runtime rejected a kernel launch */
 #define SKV_ERR_PLAN (-8)          /* inconsistent plan hints or metadata sizes */
 #define SKV_ERR_ALIGN (-9)         /* partials.acc is not 16-byte aligned */
+#define SKV_ERR_SCRATCH (-10)      /* the call needs more than the library's static scratch */
+
+/* Bytes of the library's static device scratch (one copy per GPU it runs on,
+ * held until the process ends): the partial records of the allocation-free
+ * call live there. */
+#define SKV_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum skv_dtype {
   SKV_F32 = 0,
@@ -264,6 +270,23 @@ int skv_attention_decode_splitkv(const skv_desc* d, const skv_args* a, int32_t n
                                  const skv_partials* p, void* stream);
 int skv_attention_decode_paged_splitkv(const skv_desc* d, const skv_args* a, int32_t num_splits,
                                        const skv_partials* p, void* stream);
+
+/* ---- allocation-free split-KV call -----------------------------------------
+ * For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as skv_attention_decode_paged_splitkv, same kernels and results, with
+ * the partial records in the library's static device scratch instead of
+ * caller buffers. Nothing is allocated or freed. The records of B *
+ * num_splits * Hkv slots (m, l and fp32 or bf16 acc, each region 256-byte
+ * aligned) must fit in SKV_STATIC_SCRATCH_BYTES; SKV_ERR_SCRATCH otherwise,
+ * before anything is enqueued. The first call on a device looks the scratch
+ * up on that device (a HIP symbol query; SKV_ERR_LAUNCH if it fails). Every
+ * call on one GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (other streams, other threads) race and are not allowed. No
+ * scratch content needs to start at any value: every record a call's
+ * combine reads is written by the same call's partial stage. */
+int skv_attention_decode_paged_splitkv_noalloc(const skv_desc* d, const skv_args* a, int32_t num_splits,
+                                               void* stream);
 
 /* ---- host split planner ([PA] intro, Changes) -----------------------------
  * The planner turns host-known context lengths into per-request partition

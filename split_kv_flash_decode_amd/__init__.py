@@ -93,6 +93,8 @@ EXPORTS = {
                                                     ctypes.POINTER(Partials), _c_ptr]),
     "skv_attention_decode_paged_splitkv": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32,
                                                           ctypes.POINTER(Partials), _c_ptr]),
+    "skv_attention_decode_paged_splitkv_noalloc": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args),
+                                                                  _c_i32, _c_ptr]),
     "skv_plan_meta_len": (ctypes.c_int64, [_c_i32, _c_i32]),
     "skv_plan_capacity": (ctypes.c_int, [ctypes.POINTER(PlanHints), ctypes.POINTER(_c_i32),
                                          ctypes.POINTER(_c_i32)]),
@@ -310,6 +312,14 @@ def attention_decode_paged_splitkv(desc: Desc, args: Args, num_splits: int, ws: 
     _check(lib().skv_attention_decode_paged_splitkv(ctypes.byref(desc), ctypes.byref(args), int(num_splits),
                                                     ctypes.byref(ws.struct), _stream(stream)),
            "skv_attention_decode_paged_splitkv")
+
+
+def attention_decode_paged_splitkv_noalloc(desc: Desc, args: Args, num_splits: int, stream=None):
+    """The split-KV call with its partial records in the library's static
+    device scratch (no caller buffers, nothing allocated)."""
+    _check(lib().skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(desc), ctypes.byref(args),
+                                                            int(num_splits), _stream(stream)),
+           "skv_attention_decode_paged_splitkv_noalloc")
 
 
 def attention_decode_paged_planned(desc: Desc, args: Args, plan_meta_dev: torch.Tensor, capacity: int,

@@ -248,6 +248,7 @@ const char* skv_status_str(int status) {
     case SKV_ERR_LAUNCH: return "kernel launch failed";
     case SKV_ERR_PLAN: return "inconsistent plan hints or metadata";
     case SKV_ERR_ALIGN: return "partials.acc is not 16-byte aligned";
+    case SKV_ERR_SCRATCH: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -308,6 +309,24 @@ int skv_attention_decode(const skv_desc* d, const skv_args* a, void* stream) {
 int skv_attention_decode_paged(const skv_desc* d, const skv_args* a, void* stream) {
   return single_pass(d, a, 1, stream);
 }
+
+}  // extern "C"
+
+namespace skv {
+int check_split_call(const skv_desc* d, const skv_args* a, int paged, int32_t num_splits) {
+  int rc = check_desc(d, paged);
+  if (rc) return rc;
+  rc = check_args(d, a, paged);
+  if (rc) return rc;
+  if (num_splits < 1 || num_splits > SKV_MAX_SPLITS) return SKV_ERR_SPLITS;
+  if ((int64_t)d->batch * num_splits * d->num_kv_heads * 64 > INT32_MAX) return SKV_ERR_SHAPE;
+  skv_args none;
+  memset(&none, 0, sizeof(none));
+  return impl_check(make_params(d, &none, paged, num_splits, nullptr, nullptr, 0));
+}
+}  // namespace skv
+
+extern "C" {
 
 static int split_call(const skv_desc* d, const skv_args* a, int paged, int32_t num_splits,
                       const skv_partials* p, void* stream) {

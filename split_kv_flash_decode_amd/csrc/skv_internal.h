@@ -183,4 +183,7 @@ int launch_partial_mfma(Params p, void* stream);
 int launch_combine(Params p, void* stream);
 int launch_plan_device(const PlanDev& h, const int32_t* ctx, int32_t* meta, void* stream);
 bool mfma_supported(const Params& p);
+// Host checks of a uniform split call other than its partial buffers
+// (descriptor, arguments, split count, grid limits, kernel family).
+int check_split_call(const skv_desc* d, const skv_args* a, int paged, int32_t num_splits);
 }  // namespace skv

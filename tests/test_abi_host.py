@@ -374,3 +374,20 @@ def test_matrix_core_kernel_refuses_32_bit_offset_overflow():
     assert skv.validate(desc(too_big, "mfma"), False, 0) == -6
     assert skv.validate(desc(too_big, "auto"), False, 0) == 0
     assert skv.validate(desc(too_big, "mfma", "plain"), False, 0) == 0   # plain V: 64-bit rows
+
+
+def test_noalloc_call_refuses_records_beyond_the_static_scratch():
+    """The allocation-free call checks its record bytes against the static
+    scratch before any HIP call: too many records -> SKV_ERR_SCRATCH, and the
+    usual argument errors first."""
+    L = _lib()
+    fake = 1 << 20                                        # never dereferenced: the call fails first
+    a = skv.Args(fake, fake, fake, fake, fake, fake, fake, None, fake, None)
+    d = _desc(B=200, R=4, Hq=16, Hkv=1, D=128)
+    # 200 * 256 * 1 slots x 64 rows x (128 + 2) x 4 B = 1.7 GB > 128 MiB
+    assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(a), 256, None) == -10
+    assert "static scratch" in skv.status_str(-10)
+    assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(skv.Args()), 16,
+                                                        None) == -1
+    assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(a), 0, None) == -4
+    assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(a), 257, None) == -4
