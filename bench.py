@@ -280,8 +280,13 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     """Generate the workload (or take ``problem``), run the planned step (host
     plan refresh, metadata copy, partial, combine) ``warmup`` + ``steps`` times.
 
-    ``mode`` "fused": the single-kernel split + merge instead of partial +
-    combine (its time is reported as the partial time, combine 0);
+    ``mode`` "two_stage": host plan refresh, metadata copy, partial, combine;
+    "host_plan": host plan refresh, then the planned call with the plan block
+    passed to the kernels by value (no copy; its event time is reported as
+    the partial time, combine 0); "auto": host_plan when the plan block fits
+    the kernels' argument block, else two_stage; "fused": the single-kernel
+    split + merge instead of partial + combine (its time is reported as the
+    partial time, combine 0);
     "device_plan": the plan refreshed on the GPU from the device lengths
     instead of on the host. In the timed steps only the partial kernel is
     bracketed by events (each event record adds a few microseconds to the
@@ -317,8 +322,23 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
     ws = skv.Workspace(d, plan.info.slots, dev)
     stream = torch.cuda.current_stream()
     counters = torch.zeros(spec.B * spec.Hkv, dtype=torch.int32, device=dev)
+    if mode == "auto":
+        mode = "host_plan" if plan.dev.numel() <= skv.SKV_PLAN_INLINE_MAX else "two_stage"
+    host_meta = torch.empty(plan.dev.numel(), dtype=torch.int32)
 
     def step(ev=None, refresh=True):
+        if mode == "host_plan":
+            # the plan block goes to the kernels by value: no copy, one call
+            if refresh:
+                skv.plan_fill(plan.hints, host_ctx, plan.capacity, host_meta)
+            if ev is not None:
+                ev[0].record(stream)
+            skv.attention_decode_paged_planned_host(d, a, host_meta, plan.capacity, ws)
+            if ev is not None:
+                ev[1].record(stream)
+                if len(ev) > 2:
+                    ev[2].record(stream)
+            return
         if refresh:
             if mode == "device_plan":
                 plan.refresh_device(p.ctx)
@@ -383,9 +403,11 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
             times.append(e0.elapsed_time(e1))
         cold_ms = sorted(times)[len(times) // 2]
         del flush
+    if mode == "host_plan":
+        comb_ms = [0.0]                                  # part_ms holds the whole call
     return {"ms": plain_ms if event_free_pass else wall * 1e3 / steps, "part_ms": part_ms,
             "comb_ms": comb_ms, "plan": plan, "problem": p, "cold_ms": cold_ms, "ms_excl_plan": excl_ms,
-            "output": o}
+            "output": o, "mode": mode}
 
 
 def table(args) -> int:
@@ -397,7 +419,7 @@ def table(args) -> int:
         spec = config_spec(n, block_size=bs, v_layout=vl, **over)
         small = max(spec.ctx) * spec.B < 10_000_000
         steps, warmup = (400, 50) if small else (args.steps, args.warmup)
-        r = timed_steps(spec, n, steps, warmup, event_free_pass=True)
+        r = timed_steps(spec, n, steps, warmup, event_free_pass=True, mode="auto")
         ms, part_ms, comb_ms, plan, p, cold_ms = r["ms"], r["part_ms"], r["comb_ms"], r["plan"], r["problem"], r["cold_ms"]
         tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
         print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
@@ -408,7 +430,8 @@ def table(args) -> int:
                           "page_TBps": page_tbs, "time_vs_page": round(ms * 1e3 / page_us, 4),
                           "partial_us_mean": round(sum(part_ms) / len(part_ms) * 1e3, 2),
                           "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
-                          "plan_items": plan.info.num_items, "steps": steps, "warmup": warmup}), flush=True)
+                          "plan_items": plan.info.num_items, "step_mode": r["mode"],
+                          "steps": steps, "warmup": warmup}), flush=True)
         del p
         torch.cuda.empty_cache()
     return 0
@@ -525,9 +548,9 @@ def all_configs(args) -> int:
         nbytes = spec_bytes(spec)
         unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
         alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
-        r = timed_steps(spec, n, steps, warmup, event_free_pass=True, excl_plan_pass=True)
+        r = timed_steps(spec, n, steps, warmup, event_free_pass=True, excl_plan_pass=True, mode="auto")
         part_us = sum(r["part_ms"]) / len(r["part_ms"]) * 1e3
-        row = {"config": n, "workload": workload_name(spec), "mode": "planner",
+        row = {"config": n, "workload": workload_name(spec), "mode": f"planner ({r['mode']})",
                "plan_items": r["plan"].info.num_items, "logical_bytes": nbytes,
                "us_per_step_warm": round(r["ms"] * 1e3, 2),
                "us_per_step_cold": round(r["cold_ms"] * 1e3, 2),

@@ -138,6 +138,7 @@ extern "C" {
 #define SKV_PLAN_DEVICE_MAX_BATCH 2048   /* largest batch skv_plan_refresh_device plans */
 #define SKV_MAX_SPLITS 256    /* per request ([PA] Changes: maximum of 256) */
 #define SKV_MAX_VERIFY_ROWS 256   /* query rows per request with verify masks (four mask words) */
+#define SKV_PLAN_INLINE_MAX 480   /* int32 of a plan block skv_attention_decode_paged_planned_host takes */
 /* The planner's default cap on partitions per request (max_partitions = 0):
  * a merge visits every record of a request, so past this many partitions
  * the merge costs more than the extra partial workgroups save (measured on
@@ -393,6 +394,19 @@ int skv_plan_refresh_device(const skv_plan_hints* h, const int32_t* ctx_dev, int
 int skv_attention_decode_paged_planned(const skv_desc* d, const skv_args* a,
                                        const int32_t* plan_meta, int32_t capacity_items,
                                        const skv_partials* p, void* stream);
+
+/* The same call with the plan block in HOST memory (plan_meta_host, as
+ * skv_plan_fill or skv_plan_refresh wrote it) instead of a device copy: the
+ * block travels to the kernels by value, inside their argument block, so no
+ * host-to-device copy precedes the call and the caller may refill the host
+ * buffer as soon as the call returns. For plans of at most
+ * SKV_PLAN_INLINE_MAX int32 (4 + 2 B + C; SKV_ERR_UNSUPPORTED above, e.g.
+ * B200 x 200k with C = 3200 uses the device copy); the block's header must
+ * say B and C (SKV_ERR_PLAN otherwise). Outputs are bit-identical to
+ * skv_attention_decode_paged_planned with the same plan. */
+int skv_attention_decode_paged_planned_host(const skv_desc* d, const skv_args* a,
+                                            const int32_t* plan_meta_host, int32_t capacity_items,
+                                            const skv_partials* p, void* stream);
 
 /* ---- the two stages on their own -----------------------------------------
  * skv_splitkv_partial enqueues only the partial kernel, skv_splitkv_combine

@@ -33,6 +33,7 @@ SKV_V_PLAIN, SKV_V_TRANSPOSED = 0, 1
 SKV_IMPL_AUTO, SKV_IMPL_VALU, SKV_IMPL_MFMA = 0, 1, 2
 SKV_SPLIT_ALIGN = 64
 SKV_MAX_SPLITS = 256
+SKV_PLAN_INLINE_MAX = 480
 
 _c_i32 = ctypes.c_int32
 _c_ptr = ctypes.c_void_p
@@ -104,6 +105,9 @@ EXPORTS = {
     "skv_plan_refresh": (ctypes.c_int, [ctypes.POINTER(SkvPlan), ctypes.POINTER(_c_i32)]),
     "skv_attention_decode_paged_planned": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args),
                                                           _c_ptr, _c_i32, ctypes.POINTER(Partials), _c_ptr]),
+    "skv_attention_decode_paged_planned_host": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args),
+                                                               ctypes.POINTER(_c_i32), _c_i32,
+                                                               ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_partial": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_i32,
                                            _c_ptr, ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_combine": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32,
@@ -328,6 +332,17 @@ def attention_decode_paged_planned(desc: Desc, args: Args, plan_meta_dev: torch.
                                                     plan_meta_dev.data_ptr(), int(capacity),
                                                     ctypes.byref(ws.struct), _stream(stream)),
            "skv_attention_decode_paged_planned")
+
+
+def attention_decode_paged_planned_host(desc: Desc, args: Args, plan_meta_host: torch.Tensor, capacity: int,
+                                        ws: Workspace, stream=None):
+    """The planned call with the plan block in host memory (a CPU int32
+    tensor as plan_fill wrote it), passed to the kernels by value."""
+    _need(plan_meta_host.device.type == "cpu" and plan_meta_host.dtype == torch.int32
+          and plan_meta_host.is_contiguous(), "plan_meta_host must be a contiguous CPU int32 tensor")
+    _check(lib().skv_attention_decode_paged_planned_host(
+        ctypes.byref(desc), ctypes.byref(args), ctypes.cast(plan_meta_host.data_ptr(), ctypes.POINTER(_c_i32)),
+        int(capacity), ctypes.byref(ws.struct), _stream(stream)), "skv_attention_decode_paged_planned_host")
 
 
 def splitkv_partial(desc: Desc, args: Args, paged: bool, num_splits: int, ws: Workspace,

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "skv_internal.h"
@@ -119,6 +120,44 @@ __device__ __forceinline__ int page_of(const Params& p, int b, int t) {
   return p.paged ? p.table[(int64_t)b * p.max_pages + (t >> p.bs_shift)] : 0;
 }
 
+// ---- the plan ------------------------------------------------------------------
+__device__ __forceinline__ bool planned(const Params& p) { return p.plan != nullptr || p.plan_inline; }
+
+// The plan's metadata block: in device memory, or (a plan passed by value)
+// in the kernel's own argument block, found through the kernarg segment
+// pointer (the parameter block is the kernel's first and only argument, at
+// offset 0), so the block is never copied into private memory. One generic
+// pointer for both cases keeps the scalar registers free.
+__device__ __forceinline__ const int32_t* plan_base(const Params& p) {
+  if (p.plan_inline) {
+    typedef const __attribute__((address_space(4))) char kchar;
+    kchar* blob = (kchar*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(Params, plan_blob);
+    return (const int32_t*)(const char*)blob;
+  }
+  return p.plan;
+}
+
+// Work item -> (request, split, splits of the request, record item index);
+// false for an unused plan item.
+__device__ __forceinline__ bool decode_item(const Params& p, int item, Item* it) {
+  if (planned(p)) {
+    // (values the whole workgroup shares: kept in scalar registers)
+    const int32_t* plan = plan_base(p);
+    const int w = __builtin_amdgcn_readfirstlane(plan[4 + 2 * p.B + item]);
+    if (w < 0) return false;
+    it->b = w >> 8;
+    it->s = w & 255;
+    it->S = __builtin_amdgcn_readfirstlane(plan[4 + it->b]);
+    it->slot_item = __builtin_amdgcn_readfirstlane(plan[4 + p.B + it->b]) + it->s;
+  } else {
+    it->b = item / p.num_splits;
+    it->s = item - it->b * p.num_splits;
+    it->S = p.num_splits;
+    it->slot_item = item;
+  }
+  return true;
+}
+
 __device__ __forceinline__ int clamp_ctx(const Params& p, int b) {
   int c = p.ctx[b];
   c = c < 0 ? 0 : c;
@@ -175,16 +214,6 @@ __device__ __forceinline__ int64_t qo_idx(const Params& p, int b, int j, int h, 
 __device__ __forceinline__ void row_jh(const Params& p, int g, int r, int* j, int* h) {
   *j = r / p.G;
   *h = g * p.G + (r - (r / p.G) * p.G);
-}
-
-// Merged output of query row r, d .. d + 3, of request b and KV head g from
-// the records of its S splits (slots slot0 .. slot0 + S - 1), visited in
-// increasing split order: the flash-decoding merge (tiny-llm #11 split-KV
-// design record, "Design"); h is the row's query head (for its sink).
-// x of lane K of this lane's group of four (DPP quad_perm [K, K, K, K]).
-template <int K>
-__device__ __forceinline__ float quad_lane(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xF, 0xF, true));
 }
 
 // Partial-record accumulator stores: fp32, or bf16 by round to nearest even.
@@ -265,82 +294,124 @@ __device__ __forceinline__ MergeState merge_range(const Params& p, int64_t rec0,
   return t;
 }
 
-// Merged output of query row r, d .. d + 3, of request b and KV head g from
-// the records of its S splits (slots slot0 .. slot0 + S - 1): the
-// flash-decoding merge (tiny-llm #11 split-KV design record, "Design"); h is
-// the row's query head (for its sink). Called by four adjacent lanes q = 0..3
-// together: lane q merges its quarter of the splits, then every lane takes
-// the four quarter states in order q = 0..3 (with the same step as single
-// records), so the order is fixed and the result deterministic. With at most
-// four splits every quarter holds at most one record and the sequence is the
-// per-record one; with one split the operations are those of the single-pass
-// finalize (finalize_one), so S = 1 stays bit-identical to the single pass.
+// ---- the combine of a request's records ----------------------------------------
+// The flash-decoding merge (tiny-llm #11 split-KV design record, "Design";
+// aiter #5628 "tune MTP work budgets and planned reduction", Changes: only
+// the partitions a request actually has). A request with S splits owns S
+// work items; each item gives the merge K workgroups per KV head, so the
+// request's S * K workgroups share its rho * D / 4 output units (four
+// consecutive d of one query row) whatever S is: every thread loads about
+// eight records, and a long request is merged by as many workgroups as it
+// has splits. Inside a workgroup, L lanes (a power of two) share a unit and
+// take consecutive runs of its splits in increasing order; their states are
+// then merged by a fixed butterfly, each pair in split order, so the result
+// does not depend on timing (deterministic), only on (S, K, rho, D).
+
+constexpr int kMergeThreads = 256;
+
+// Workgroups per (item, KV head) of the combine: about eight record loads per
+// thread (2048 units per workgroup of 256 threads).
+SKV_HD int merge_wgs_per_item(int rho, int D) { return (rho * (D / 4) + 2047) / 2048; }
+
+// Merge of two states, a holding earlier splits than b.
+__device__ __forceinline__ MergeState merge_pair(const MergeState& a, const MergeState& b) {
+  if (!(b.L > 0.0f)) return a;
+  if (!(a.L > 0.0f)) return b;
+  const float M = fmaxf(a.M, b.M);
+  const float wa = fexp2(a.M - M), wb = fexp2(b.M - M);
+  MergeState t;
+  t.M = M;
+  t.L = wa * a.L + wb * b.L;
+  t.a[0] = wa * a.a[0] + wb * b.a[0];
+  t.a[1] = wa * a.a[1] + wb * b.a[1];
+  t.a[2] = wa * a.a[2] + wb * b.a[2];
+  t.a[3] = wa * a.a[3] + wb * b.a[3];
+  return t;
+}
+
+__device__ __forceinline__ MergeState shfl_state(const MergeState& s, int off) {
+  MergeState o;
+  o.M = __shfl_xor(s.M, off, 64);
+  o.L = __shfl_xor(s.L, off, 64);
+  o.a[0] = __shfl_xor(s.a[0], off, 64);
+  o.a[1] = __shfl_xor(s.a[1], off, 64);
+  o.a[2] = __shfl_xor(s.a[2], off, 64);
+  o.a[3] = __shfl_xor(s.a[3], off, 64);
+  return o;
+}
+
+// Part w (of S * K) of the merge of request b, KV head g, whose S records
+// start at slot item slot0, as thread t (0 <= t < 256) of a 256-thread group:
+// output units [w U / (S K), (w + 1) U / (S K)), U = rho * D / 4. Lanes of one
+// unit are consecutive threads, so a group of 64 threads (a wave) holds whole
+// units and may run on its own.
 template <bool RBF>
-__device__ __forceinline__ floatx4 merge_splits4(const Params& p, int g, int r, int d, int h, int S, int slot0,
-                                                 int q) {
-  const int64_t rs = (int64_t)p.Hkv * p.rho;       // record stride between splits
-  const int64_t rec0 = (int64_t)slot0 * rs + (int64_t)g * p.rho + r;
-  const int c = (S + 3) >> 2;
-  const int sb = q * c < S ? q * c : S, se = (q + 1) * c < S ? (q + 1) * c : S;
-  // (batch size from the quarter length, the same for every lane of a
-  // request: no loads wasted on short quarters; batches of at most eight
-  // keep the register count, and so the occupancy, up)
-  const MergeState part =
-      c <= 4 ? merge_range<4, RBF>(p, rec0, rs, d, sb, se) : merge_range<8, RBF>(p, rec0, rs, d, sb, se);
-  MergeState t{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}};
-  merge_absorb(t, quad_lane<0>(part.M), quad_lane<0>(part.L),
-               floatx4{quad_lane<0>(part.a[0]), quad_lane<0>(part.a[1]), quad_lane<0>(part.a[2]), quad_lane<0>(part.a[3])});
-  merge_absorb(t, quad_lane<1>(part.M), quad_lane<1>(part.L),
-               floatx4{quad_lane<1>(part.a[0]), quad_lane<1>(part.a[1]), quad_lane<1>(part.a[2]), quad_lane<1>(part.a[3])});
-  merge_absorb(t, quad_lane<2>(part.M), quad_lane<2>(part.L),
-               floatx4{quad_lane<2>(part.a[0]), quad_lane<2>(part.a[1]), quad_lane<2>(part.a[2]), quad_lane<2>(part.a[3])});
-  merge_absorb(t, quad_lane<3>(part.M), quad_lane<3>(part.L),
-               floatx4{quad_lane<3>(part.a[0]), quad_lane<3>(part.a[1]), quad_lane<3>(part.a[2]), quad_lane<3>(part.a[3])});
-  floatx4 out = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (t.M != -INFINITY) {
-    float L = t.L;
-    floatx4 a = t.a;
-    if (p.has_sink) {
-      const float s2 = p.sinks[h] * kLog2e;
-      const float M2 = fmaxf(t.M, s2);
-      const float sc = fexp2(t.M - M2);
-      L *= sc;
-      a[0] *= sc;
-      a[1] *= sc;
-      a[2] *= sc;
-      a[3] *= sc;
-      L += fexp2(s2 - M2);
+__device__ __forceinline__ void merge_part(const Params& p, int b, int g, int S, int slot0, int w, int K, int t) {
+  const int tpr = p.D >> 2;
+  const int64_t U = (int64_t)p.rho * tpr;
+  const int64_t parts = (int64_t)S * K;
+  const int u0 = (int)(w * U / parts), u1 = (int)((w + 1) * U / parts);
+  const int nu = u1 - u0;
+  if (nu <= 0) return;
+  int L = 1;                                     // lanes per unit: the most that keep one pass
+  while (L < 64 && 2 * L * nu <= kMergeThreads) L <<= 1;
+  const int q = t & (L - 1);
+  const int c = (S + L - 1) / L;                 // splits per lane
+  const int sb = q * c < S ? q * c : S, se = q * c + c < S ? q * c + c : S;
+  const int64_t rs = (int64_t)p.Hkv * p.rho;     // record stride between splits
+  for (int u = u0 + t / L; u < u1; u += kMergeThreads / L) {
+    const int r = u / tpr, d = 4 * (u - r * tpr);
+    const int64_t rec0 = (int64_t)slot0 * rs + (int64_t)g * p.rho + r;
+    MergeState st = c <= 4 ? merge_range<4, RBF>(p, rec0, rs, d, sb, se) : merge_range<8, RBF>(p, rec0, rs, d, sb, se);
+    for (int off = L >> 1; off > 0; off >>= 1) {
+      const MergeState o = shfl_state(st, off);
+      st = (q & off) ? merge_pair(o, st) : merge_pair(st, o);
     }
-    const float inv = 1.0f / (L + 1e-9f);
-    out[0] = a[0] * inv;
-    out[1] = a[1] * inv;
-    out[2] = a[2] * inv;
-    out[3] = a[3] * inv;
+    if (q == 0) {
+      int j, h;
+      row_jh(p, g, r, &j, &h);
+      floatx4 out = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (st.L > 0.0f) {
+        float L2 = st.L;
+        floatx4 acc = st.a;
+        if (p.has_sink) {
+          const float s2 = p.sinks[h] * kLog2e;
+          const float M2 = fmaxf(st.M, s2);
+          const float sc = fexp2(st.M - M2);
+          L2 *= sc;
+          acc[0] *= sc;
+          acc[1] *= sc;
+          acc[2] *= sc;
+          acc[3] *= sc;
+          L2 += fexp2(s2 - M2);
+        }
+        const float inv = 1.0f / (L2 + 1e-9f);
+        out[0] = acc[0] * inv;
+        out[1] = acc[1] * inv;
+        out[2] = acc[2] * inv;
+        out[3] = acc[3] * inv;
+      }
+      store_o4(p, qo_idx(p, b, j, h, d), out);
+    }
   }
-  return out;
 }
 
 // Single-kernel split + merge (tiny-llm #11 split-KV design record, points
 // for reviewer decision, Q1): called by every workgroup of a partial kernel
 // after it wrote its records. The workgroups of one (request, KV head) count
-// themselves on a device-scope counter; the last one to arrive merges all of
-// that pair's rows in fixed split order (so the output does not depend on
-// which workgroup was last) and resets the counter to zero for the next call.
-// One agent-scope release fence per workgroup before it counts (after a
-// barrier, so it covers every wave's stores), an acquire fence in the merging
-// workgroup after: the records of workgroups on other XCDs are then visible
-// to it.
-__device__ __forceinline__ void fused_merge_tail(const Params& p, int b, int g, int nthreads) {
+// themselves on a device-scope counter; the last one to arrive runs every
+// part of that pair's merge (merge_part for w = 0 .. S K - 1, with the same
+// thread numbering as the combine kernel, so the output has the same bits
+// whichever workgroup arrives last) and resets the counter to zero for the
+// next call. One agent-scope release fence per workgroup before it counts
+// (after a barrier, so it covers every wave's stores), an acquire fence in
+// the merging workgroup after: the records of workgroups on other XCDs are
+// then visible to it. it is the calling workgroup's decoded work item;
+// nthreads is a multiple of 64.
+__device__ __forceinline__ void fused_merge_tail(const Params& p, const Item& it, int g, int nthreads) {
   __shared__ int last_s;
   const int tid = threadIdx.x;
-  int S, slot0;
-  if (p.plan) {
-    S = p.plan[4 + b];
-    slot0 = p.plan[4 + p.B + b];
-  } else {
-    S = p.num_splits;
-    slot0 = b * S;
-  }
+  const int b = it.b, S = it.S, slot0 = it.slot_item - it.s;   // the request's split 0
   __syncthreads();                                 // the workgroup's record stores are done
   if (tid == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and visible device-wide
@@ -353,15 +424,14 @@ __device__ __forceinline__ void fused_merge_tail(const Params& p, int b, int g, 
   __syncthreads();
   if (!last_s) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int tpr = p.D >> 2;                        // four d per output, four lanes per output
-  for (int idx = tid; idx < 4 * p.rho * tpr; idx += nthreads) {
-    const int o = idx >> 2, q = idx & 3;
-    const int r = o / tpr, d = 4 * (o - r * tpr);
-    int j, h;
-    row_jh(p, g, r, &j, &h);
-    const floatx4 v = p.rec_bf16 ? merge_splits4<true>(p, g, r, d, h, S, slot0, q)
-                                 : merge_splits4<false>(p, g, r, d, h, S, slot0, q);
-    if (q == 0) store_o4(p, qo_idx(p, b, j, h, d), v);
+  const int K = merge_wgs_per_item(p.rho, p.D);
+  const int total = S * K * kMergeThreads;
+  for (int vt = tid; vt < total; vt += nthreads) {
+    const int w = vt / kMergeThreads, t = vt - w * kMergeThreads;
+    if (p.rec_bf16)
+      merge_part<true>(p, b, g, S, slot0, w, K, t);
+    else
+      merge_part<false>(p, b, g, S, slot0, w, K, t);
   }
 }
 

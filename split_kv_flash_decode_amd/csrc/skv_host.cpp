@@ -493,6 +493,31 @@ int skv_attention_decode_paged_planned(const skv_desc* d, const skv_args* a,
   return skv::launch_combine(prm, stream);
 }
 
+int skv_attention_decode_paged_planned_host(const skv_desc* d, const skv_args* a,
+                                            const int32_t* plan_meta_host, int32_t capacity_items,
+                                            const skv_partials* p, void* stream) {
+  int rc = check_desc(d, 1);
+  if (rc) return rc;
+  rc = check_args(d, a, 1);
+  if (rc) return rc;
+  if (!plan_meta_host) return SKV_ERR_NULL;
+  if (capacity_items < d->batch) return SKV_ERR_CAPACITY;
+  const int64_t n = skv_plan_meta_len(d->batch, capacity_items);
+  if (n > SKV_PLAN_INLINE_MAX) return SKV_ERR_UNSUPPORTED;
+  if (plan_meta_host[0] != d->batch || plan_meta_host[1] != capacity_items) return SKV_ERR_PLAN;
+  rc = check_partials(d, p, (int64_t)capacity_items * d->num_kv_heads);
+  if (rc) return rc;
+  skv::Params prm = make_params(d, a, 1, capacity_items, nullptr, p, 0);
+  prm.n_items = capacity_items;
+  prm.plan_inline = 1;
+  memcpy(prm.plan_blob, plan_meta_host, (size_t)n * sizeof(int32_t));
+  rc = impl_check(prm);
+  if (rc) return rc;
+  rc = run_partial(prm, stream);
+  if (rc) return rc;
+  return skv::launch_combine(prm, stream);
+}
+
 int skv_splitkv_partial(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
                         const int32_t* plan_meta, const skv_partials* p, void* stream) {
   int rc = check_desc(d, paged);

@@ -41,6 +41,11 @@ struct Params {
   int32_t row_groups;    // row groups per (item, KV head)
   int32_t q_dtype, kv_dtype, v_layout, block_size, impl;
   int32_t rec_bf16;      // 1: record acc in bf16
+  // A plan passed by value (skv_attention_decode_paged_planned_host): the
+  // metadata block is plan_blob itself, read from the kernel's argument
+  // block; plan is then nullptr. Last, so the fields above keep their offsets.
+  int32_t plan_inline;
+  int32_t plan_blob[SKV_PLAN_INLINE_MAX];
 };
 
 // Resolved planner hints for the device-side planner.
@@ -152,27 +157,11 @@ SKV_HD bool mfma_offsets_fit(int paged, int v_layout, int D, int kv_cap, int kv_
   return (long long)D * kv_cap * kv_bytes < (1ll << 31);
 }
 
-// Work item -> (request, split, splits of the request, record item index).
+// Work item -> (request, split, splits of the request, record item index);
+// decoded by decode_item in skv_device.h.
 struct Item {
   int b, s, S, slot_item;
 };
-
-SKV_HD bool decode_item(const Params& p, int item, Item* it) {
-  if (p.plan) {
-    int w = p.plan[4 + 2 * p.B + item];
-    if (w < 0) return false;
-    it->b = w >> 8;
-    it->s = w & 255;
-    it->S = p.plan[4 + it->b];
-    it->slot_item = p.plan[4 + p.B + it->b] + it->s;
-  } else {
-    it->b = item / p.num_splits;
-    it->s = item - it->b * p.num_splits;
-    it->S = p.num_splits;
-    it->slot_item = item;
-  }
-  return true;
-}
 
 }  // namespace skv
 

@@ -42,7 +42,12 @@
 //    fp8 high part and an fp8 residual with power-of-two block scales, which
 //    reproduces every bf16 element within 2^13 of its block maximum exactly;
 //    these products accumulate at about 2^-14 of the sum of their magnitudes
-//    (measured), not at fp32. INT8 and BF16 K convert to bf16 (exactly) for
+//    (measured), not at fp32. INT8 K with a bf16 query feeds the int8 matrix
+//    cores directly (v_mfma_i32_32x32x32_i8): Q is split once per workgroup,
+//    per row, into two int8 parts with one power-of-two scale (every bf16
+//    element within 2^7 of the row's maximum exactly, the rest within 2^-14
+//    of the maximum), and the two int32 sums combine exactly before one
+//    conversion per logit. BF16 K converts to bf16 (no-op) for
 //    v_mfma_f32_32x32x16_bf16. With an fp16 query, INT8 and FP8 K convert to
 //    fp16 (exactly) for v_mfma_f32_32x32x16_f16, the query keeping all its
 //    bits. V codes always convert to bf16 exactly. The
@@ -67,7 +72,9 @@ namespace skv {
 namespace {
 
 typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -224,9 +231,14 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // format (bf16 or fp16) and multiplied on the 16-bit matrix cores. P V is
   // always a bf16 product.
   constexpr bool F8QK = __is_same(KT, FP8) && __is_same(QT, BF16);
+  // INT8 K with a bf16 query: S^T = K Q^T runs on the int8 matrix cores
+  // (32x32x32, exact int32 sums), Q split once per workgroup into two int8
+  // parts with one power-of-two scale per row.
+  constexpr bool I8QK = __is_same(KT, I8) && __is_same(QT, BF16);
   typedef typename QOperand<QT>::type qop;
-  constexpr int QS8 = D + 16;                    // LDS row stride of the fp8 Q parts, padded
-  constexpr int QBYTES = F8QK ? 2 * ROWS * QS8 + ROWS * (D / 32) * 2 : ROWS * QS * 2;
+  constexpr int QS8 = D + 16;                    // LDS row stride of the 8-bit Q parts, padded
+  constexpr int QBYTES = F8QK ? 2 * ROWS * QS8 + ROWS * (D / 32) * 2
+                              : (I8QK ? 2 * ROWS * QS8 + ROWS * 4 : ROWS * QS * 2);
   constexpr int BUDGET = 156 * 1024;
   constexpr int NS0 = (BUDGET - QBYTES) / (4 * STAGE);
   constexpr int NS = NS0 > 4 ? 4 : (NS0 < 2 ? 2 : NS0);   // ring stages per key stream
@@ -302,6 +314,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   uint8_t* qh_s = reinterpret_cast<uint8_t*>(smem + SMEM0);   // fp8 Q parts (F8QK)
   uint8_t* ql_s = qh_s + ROWS * QS8;
   uint8_t* qe_s = ql_s + ROWS * QS8;             // [row][32-d block]: E8M0 scales of both parts
+  float* qr_s = reinterpret_cast<float*>(ql_s + ROWS * QS8);   // I8QK: [row] scale 2^(e - 7)
   // This wave's query rows: rbase + 32 rh + [0, 32); lane i32 owns one.
   const int wrow0 = rbase + 32 * rh;
   int vlo = 0, vhi = 0;
@@ -496,7 +509,12 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   u32x4 qa[KS8][2], qb[KS8][2];
   constexpr int KPC = 16 / (8 * EB);              // k-steps per 16-byte chunk
   constexpr int KS = NCH * KPC;                   // k-steps of 16 d
-  qop qf[F8QK ? 1 : KS];
+  qop qf[(F8QK || I8QK) ? 1 : KS];
+  // int8 path: k-step ks (32 d) of lane (i32, hh) covers the 16 d
+  // [hh D/2 + 16 ks, +16) of K row tau(i32) and of Q row 32 rh + i32
+  constexpr int KSI = D / 32;
+  u32x4 qih[I8QK ? KSI : 1], qil[I8QK ? KSI : 1];
+  float qrs = 1.0f;                               // this lane's row scale 2^(e - 7)
   // Stage the group's query rows in LDS and read this lane's operand parts
   // back (called once the first blocks' loads are in flight, so their
   // latency overlaps the query loads).
@@ -562,6 +580,68 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         qe_s[(row * (D / 32) + blk) * 2] = (uint8_t)(e + 127);
         qe_s[(row * (D / 32) + blk) * 2 + 1] = (uint8_t)(e - 4 + 127);
       }
+    } else if constexpr (I8QK) {
+      // Per row: x = q 2^-e with max |x| in [64, 128); hi = rne(x) clamped to
+      // [-128, 127], lo = rne(128 (x - hi)), |lo| <= 64, so x = hi + lo / 128
+      // exactly for every element within 2^7 of the row's maximum (and within
+      // 2^-8 of it otherwise: 2^-14 of the maximum). Thread (row, 32-d block)
+      // converts its block; the row's maximum comes from a shuffle over the
+      // D / 32 consecutive threads of the row.
+      constexpr int NB = D / 32;
+      for (int idx = tid; idx < ROWS * NB; idx += NT) {
+        const int row = idx / NB, blk = idx - row * NB;
+        const int r = rbase + row;
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+        if (r < p.rho) {
+          int j, hq;
+          row_jh(p, g, r, &j, &hq);
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const u32x4 w = ld16(src + 8 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
+              x[8 * u + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            }
+          }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+        for (int o = 1; o < NB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        int e = 0;
+        if (amax > 0.0f) e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 6;
+        e = e < -100 ? -100 : (e > 127 ? 127 : e);
+        const float sc = __builtin_ldexpf(1.0f, -e);
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint32_t hb = 0, lb = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = x[4 * k + i] * sc;
+            float hi = __builtin_rintf(a);
+            hi = fminf(fmaxf(hi, -128.0f), 127.0f);
+            const float lo = __builtin_rintf(128.0f * (a - hi));
+            hb |= ((uint32_t)(int32_t)hi & 0xFFu) << (8 * i);
+            lb |= ((uint32_t)(int32_t)lo & 0xFFu) << (8 * i);
+          }
+          hw[k] = hb;
+          lw[k] = lb;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          *reinterpret_cast<u32x4*>(&qh_s[row * QS8 + 32 * blk + 16 * u]) =
+              u32x4{hw[4 * u], hw[4 * u + 1], hw[4 * u + 2], hw[4 * u + 3]};
+          *reinterpret_cast<u32x4*>(&ql_s[row * QS8 + 32 * blk + 16 * u]) =
+              u32x4{lw[4 * u], lw[4 * u + 1], lw[4 * u + 2], lw[4 * u + 3]};
+        }
+        if (blk == 0) qr_s[row] = __builtin_ldexpf(1.0f, e - 7);
+      }
     } else {
       for (int idx = tid; idx < ROWS * (D / 8); idx += NT) {
         const int row = idx / (D / 8), c8 = idx - row * (D / 8);
@@ -576,7 +656,15 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       }
     }
     __syncthreads();
-    if constexpr (!F8QK) {
+    if constexpr (I8QK) {
+      const int qrow = (32 * rh + i32) * QS8 + hh * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) {
+        qih[ks] = *reinterpret_cast<const u32x4*>(&qh_s[qrow + 16 * ks]);
+        qil[ks] = *reinterpret_cast<const u32x4*>(&ql_s[qrow + 16 * ks]);
+      }
+      qrs = qr_s[32 * rh + i32];
+    } else if constexpr (!F8QK) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
         qf[kk] = __builtin_bit_cast(qop, *reinterpret_cast<const u32x4*>(&q_s[qoff0 + 8 * kk]));
@@ -628,6 +716,22 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bh, ks == 0 ? floatx16{} : s, 0, 0, 0, 127, 0, qsh[ks]);
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bl, s, 0, 0, 0, 127, 0, qsl[ks]);
       }
+    } else if constexpr (I8QK) {
+      // int8 codes straight from LDS; S = (S_hi << 7) + S_lo is exact (|S| < 2^30)
+      u32x4 kc[KSI];
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) kc[ks] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ ks) * 16));
+      i32x16 sh, sl;
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) {
+        const v4i32 a = __builtin_bit_cast(v4i32, kc[ks]);
+        sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qih[ks]), ks == 0 ? i32x16{} : sh,
+                                                   0, 0, 0);
+        sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qil[ks]), ks == 0 ? i32x16{} : sl,
+                                                   0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = (float)((sh[v] << 7) + sl[v]);
     } else {
     // all operand reads first, so that their latency overlaps instead of
     // stalling each product
@@ -719,7 +823,16 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         asm volatile("" : "+v"(n));
         xv = ((lane & 15) < n) ? xv : 0.0f;
       }
-      row_bcast16(xk, c, std::make_integer_sequence<int, 16>{});
+      if constexpr (I8QK) {
+        // the query row's scale 2^(e - 7) rides on the broadcast (v_mul_f32_dpp)
+        float qr[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) qr[v] = qrs;
+        row_bcast_mul8<0>(xk, qr, c);
+        row_bcast_mul8<8>(xk, qr, c);
+      } else {
+        row_bcast16(xk, c, std::make_integer_sequence<int, 16>{});
+      }
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) c[v] = p.scale_log2;
@@ -970,7 +1083,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         p.pl[rec] = fin_s[rr][1];
       }
     }
-    if (p.counters) fused_merge_tail(p, b, g, NT);
+    if (p.counters) fused_merge_tail(p, it, g, NT);
   }
 }
 

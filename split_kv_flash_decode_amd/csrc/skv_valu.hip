@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64) void partial_valu(Params p) {
 #pragma unroll
       for (int k = 0; k < DPL; ++k) store_rec1(p, rec * D + lane + 64 * k, acc[rr][k]);
     }
-    if (p.counters) fused_merge_tail(p, b, g, 64);
+    if (p.counters) fused_merge_tail(p, it, g, 64);
   }
 }
 

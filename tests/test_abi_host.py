@@ -391,3 +391,33 @@ def test_noalloc_call_refuses_records_beyond_the_static_scratch():
                                                         None) == -1
     assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(a), 0, None) == -4
     assert L.skv_attention_decode_paged_splitkv_noalloc(ctypes.byref(d), ctypes.byref(a), 257, None) == -4
+
+
+def test_host_plan_call_checks_size_and_header_before_launching():
+    """skv_attention_decode_paged_planned_host: plans above SKV_PLAN_INLINE_MAX
+    int32 are refused (the B200 x 200k plan is 4 + 400 + 3200), and a block
+    whose header does not say (B, C) is refused; nothing is launched."""
+    L = _lib()
+    fake = 1 << 20
+    a = skv.Args(fake, fake, fake, fake, fake, fake, fake, None, fake, None)
+    p = skv.Partials(4096, 4096, 4096, 1 << 30)
+    d = _desc(B=200, R=4, Hq=16, Hkv=1, D=128)
+    big = torch.zeros(skv.plan_meta_len(200, 3200), dtype=torch.int32)
+    big[0], big[1] = 200, 3200
+    ptr = ctypes.cast(big.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    assert L.skv_attention_decode_paged_planned_host(ctypes.byref(d), ctypes.byref(a), ptr, 3200,
+                                                     ctypes.byref(p), None) == -6
+    d = _desc(B=16, R=4, Hq=16, Hkv=1, D=128)
+    h = skv.plan_hints(16, 4, 1)
+    ctx = [200000] + [1024] * 15
+    cap = skv.plan_capacity(h, ctx)
+    meta = torch.zeros(skv.plan_meta_len(16, cap), dtype=torch.int32)
+    skv.plan_fill(h, ctx, cap, meta)
+    assert meta.numel() <= 480
+    bad = meta.clone()
+    bad[1] = cap + 1                                      # header says another capacity
+    ptr = ctypes.cast(bad.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+    assert L.skv_attention_decode_paged_planned_host(ctypes.byref(d), ctypes.byref(a), ptr, cap,
+                                                     ctypes.byref(p), None) == -8
+    assert L.skv_attention_decode_paged_planned_host(ctypes.byref(d), ctypes.byref(a), None, cap,
+                                                     ctypes.byref(p), None) == -1
