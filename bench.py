@@ -580,6 +580,72 @@ def all_configs(args) -> int:
     return 0
 
 
+def ceiling(args) -> int:
+    """The partial kernel against the read-only gather with its memory pattern
+    (skv_gather_ceiling) on the same workload and plan, interleaved in one
+    process: HIP events around batches of launches of each, means per launch,
+    as algorithmic bytes per second and as a fraction of 8 TB/s. The gather's
+    rate is what this paged layout allows the partial kernel's loads."""
+    import statistics
+
+    import torch
+
+    import split_kv_flash_decode_amd as skv
+    from skvgen import config_spec, make_problem
+
+    over = {}
+    if args.block_size:
+        over["block_size"] = args.block_size
+    if args.v_layout:
+        over["v_layout"] = args.v_layout
+    spec = config_spec(args.config, **over)
+    dev = torch.device("cuda:0")
+    p = make_problem(spec, seed=args.seed, device=dev)
+    o = torch.empty_like(p.q)
+    d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
+                      window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
+    a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
+                      page_table=p.page_table, sinks=p.sinks)
+    hints = skv.plan_hints_for(d, True, partitions_per_request=spec.partitions_per_request)
+    plan = skv.Plan(hints, list(spec.ctx), dev)
+    ws = skv.Workspace(d, plan.info.slots, dev)
+    sink = torch.empty(plan.capacity * spec.Hkv, dtype=torch.int32, device=dev)
+
+    def part():
+        skv.splitkv_partial(d, a, True, plan.capacity, ws, plan_meta_dev=plan.dev)
+
+    def gath():
+        skv.gather_ceiling(d, a, plan.capacity, sink, plan_meta_dev=plan.dev)
+
+    inner = max(1, args.steps // 10)
+    for _ in range(args.warmup):
+        part()
+        gath()
+    torch.cuda.synchronize()
+    t = {"partial": [], "gather": []}
+    for _ in range(10):
+        for name, fn in (("partial", part), ("gather", gath)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(inner):
+                fn()
+            e1.record()
+            e1.synchronize()
+            t[name].append(e0.elapsed_time(e1) * 1e3 / inner)
+    unit_bytes = 2 * spec.D * _DT[spec.kv_dtype] + (8 if spec.kv_dtype in ("int8", "fp8") else 0)
+    alg = unit_bytes * sum(int(c) for c in spec.ctx) * spec.Hkv
+    row = {"workload": workload_name(spec), "algorithmic_bytes_per_launch": alg, "launches_each": 10 * inner}
+    for name in ("partial", "gather"):
+        us = statistics.mean(t[name])
+        row[f"{name}_us_mean"] = round(us, 2)
+        row[f"{name}_us_median"] = round(statistics.median(t[name]), 2)
+        row[f"{name}_GBps"] = round(alg / (us * 1e-6) / 1e9, 1)
+        row[f"{name}_frac_of_8TBps"] = round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    row["partial_share_of_gather_ceiling"] = round(row["gather_us_mean"] / row["partial_us_mean"], 4)
+    print(json.dumps(row), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,6 +664,9 @@ def main(argv=None) -> int:
     ap.add_argument("--next", action="store_true",
                     help="time the adjacent variants (fp16 Q/O, bf16 records, fused call, device "
                          "plan refresh, verify masks) against the default call on the same workloads")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time the partial kernel against the read-only gather with its memory pattern "
+                         "(skv_gather_ceiling) on the same workload, interleaved")
     ap.add_argument("--all", action="store_true",
                     help="per-workload table: the five workloads (planner step) and the uniform split "
                          "counts they name, warm / cache-cold / plan-excluded time per step")
@@ -609,7 +678,7 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    side_mode = args.calibrate_copy or args.next or args.table or args.all
+    side_mode = args.calibrate_copy or args.next or args.table or args.all or args.ceiling
     pool = None
     if not side_mode and not args.no_cpu_baseline:
         # the oracle's worker processes start before anything touches the GPU
@@ -637,6 +706,8 @@ def main(argv=None) -> int:
         return table(args)
     if args.all:
         return all_configs(args)
+    if args.ceiling:
+        return ceiling(args)
     overrides = {}
     if args.block_size:
         overrides["block_size"] = args.block_size

@@ -433,6 +433,22 @@ int skv_splitkv_combine(const skv_desc* d, const skv_args* a, int32_t num_splits
 int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32_t num_splits,
                       const int32_t* plan_meta, const skv_partials* p, int32_t* counters, void* stream);
 
+/* ---- measurement: the read ceiling of a paged layout -----------------------
+ * Not part of the attention path. Reads exactly the K and V codes and scales
+ * a paged split-KV call with these arguments reads (the effective bytes of
+ * [PA] Performance, bandwidth note), with the matrix-core partial kernel's
+ * memory pattern: one workgroup per (work item, KV head), four key streams of
+ * 32-key blocks, page-table reads per 16-key group, 16-byte-per-lane
+ * direct-to-LDS loads of whole rows, the same ring depth, waits and
+ * barriers, and no arithmetic. Its time is the floor those loads put under
+ * the partial kernel. Work items as skv_splitkv_partial (plan_meta NULL:
+ * uniform num_splits; else the device plan block, num_splits = its C).
+ * sink: DEVICE uint32 [sink_len] >= items * Hkv (one value per workgroup,
+ * overwritten). Paged calls with block_size >= 16 and 8-bit codes, or bf16
+ * codes at D <= 128; SKV_ERR_UNSUPPORTED otherwise. */
+int skv_gather_ceiling(const skv_desc* d, const skv_args* a, int32_t num_splits, const int32_t* plan_meta,
+                       uint32_t* sink, int64_t sink_len, void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

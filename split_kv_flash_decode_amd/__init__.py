@@ -114,6 +114,8 @@ EXPORTS = {
                                            _c_ptr, ctypes.POINTER(Partials), _c_ptr]),
     "skv_splitkv_fused": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_i32,
                                          _c_ptr, ctypes.POINTER(Partials), _c_ptr, _c_ptr]),
+    "skv_gather_ceiling": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Args), _c_i32, _c_ptr, _c_ptr,
+                                          ctypes.c_int64, _c_ptr]),
     "skv_plan_refresh_device": (ctypes.c_int, [ctypes.POINTER(PlanHints), _c_ptr, _c_i32, _c_ptr,
                                                ctypes.c_int64, _c_ptr]),
     "skv_plan_hints_for_desc": (ctypes.c_int, [ctypes.POINTER(Desc), _c_i32, ctypes.POINTER(PlanHints)]),
@@ -369,6 +371,16 @@ def splitkv_fused(desc: Desc, args: Args, paged: bool, num_splits: int, ws: Work
                                    _ptr(plan_meta_dev), ctypes.byref(ws.struct), _ptr(counters),
                                    _stream(stream)),
            "skv_splitkv_fused")
+
+
+def gather_ceiling(desc: Desc, args: Args, num_splits: int, sink: torch.Tensor,
+                   plan_meta_dev: Optional[torch.Tensor] = None, stream=None):
+    """Measurement only: the read-only gather with the partial kernel's memory
+    pattern (sink: int32/uint32 device tensor of at least items * Hkv)."""
+    _need(sink.is_cuda and sink.dtype in (torch.int32, torch.uint32) and sink.is_contiguous(),
+          "sink must be a contiguous 32-bit device tensor")
+    _check(lib().skv_gather_ceiling(ctypes.byref(desc), ctypes.byref(args), int(num_splits), _ptr(plan_meta_dev),
+                                    _ptr(sink), int(sink.numel()), _stream(stream)), "skv_gather_ceiling")
 
 
 def plan_meta_len(batch: int, capacity: int) -> int:

@@ -25,7 +25,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libskv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["skv_mfma.hip", "skv_valu.hip", "skv_combine.hip", "skv_plan.hip", "skv_noalloc.hip"]
+HIP_SOURCES = ["skv_mfma.hip", "skv_valu.hip", "skv_combine.hip", "skv_plan.hip", "skv_noalloc.hip",
+               "skv_ceiling.hip"]
 CPP_SOURCES = ["skv_host.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]

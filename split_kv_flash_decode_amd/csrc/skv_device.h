@@ -120,6 +120,41 @@ __device__ __forceinline__ int page_of(const Params& p, int b, int t) {
   return p.paged ? p.table[(int64_t)b * p.max_pages + (t >> p.bs_shift)] : 0;
 }
 
+// ---- direct-to-LDS loads ----------------------------------------------------------
+// Wait until at most n vector-memory operations of this wave are outstanding.
+// Direct-to-LDS loads count in vmcnt; the compiler does not order later LDS
+// reads after them, so every stage is consumed after an explicit wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// One direct-to-LDS load per lane (16 or 4 bytes): lane l's bytes land at
+// lds + l * size. Issued as inline assembly so that the compiler neither
+// reorders LDS reads around it nor adds its own (draining) waits; every
+// consumer waits with wait_vm.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Page-table entry read through the constant address space: the table is
+// read-only for the whole call, so uniform reads become scalar loads.
+__device__ __forceinline__ int cload(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 // ---- the plan ------------------------------------------------------------------
 __device__ __forceinline__ bool planned(const Params& p) { return p.plan != nullptr || p.plan_inline; }
 

@@ -619,6 +619,28 @@ int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32
   return run_partial(prm, stream);
 }
 
+int skv_gather_ceiling(const skv_desc* d, const skv_args* a, int32_t num_splits, const int32_t* plan_meta,
+                       uint32_t* sink, int64_t sink_len, void* stream) {
+  int rc = check_desc(d, 1);
+  if (rc) return rc;
+  rc = check_args(d, a, 1);
+  if (rc) return rc;
+  if (!sink) return SKV_ERR_NULL;
+  if (plan_meta) {
+    if (num_splits < d->batch) return SKV_ERR_CAPACITY;
+  } else if (num_splits < 1 || num_splits > SKV_MAX_SPLITS) {
+    return SKV_ERR_SPLITS;
+  }
+  const int64_t items = plan_meta ? num_splits : (int64_t)d->batch * num_splits;
+  if (items * d->num_kv_heads > INT32_MAX) return SKV_ERR_SHAPE;
+  if (sink_len < items * d->num_kv_heads) return SKV_ERR_CAPACITY;
+  const bool eight = d->kv_dtype == SKV_INT8 || d->kv_dtype == SKV_FP8_E4M3;
+  if (d->block_size < 16 || !(eight || (d->kv_dtype == SKV_BF16 && d->head_dim <= 128)))
+    return SKV_ERR_UNSUPPORTED;
+  skv::Params prm = make_params(d, a, 1, num_splits, plan_meta, nullptr, 0);
+  return skv::launch_gather_ceiling(prm, sink, stream);
+}
+
 int skv_splitkv_combine(const skv_desc* d, const skv_args* a, int32_t num_splits,
                         const int32_t* plan_meta, const skv_partials* p, void* stream) {
   int rc = check_desc(d, -1);

@@ -65,6 +65,7 @@ constexpr int kSplitAlign = SKV_SPLIT_ALIGN;
 // Lazy rescaling: the running reference maximum is only raised when a new
 // logit exceeds it by more than this many powers of two.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleLimit = 256.0f;   // 2^kRescaleSlack: the largest probability kept
 
 // Host + device helpers --------------------------------------------------------
 
@@ -171,6 +172,7 @@ int launch_partial_valu(Params p, void* stream);
 int launch_partial_mfma(Params p, void* stream);
 int launch_combine(Params p, void* stream);
 int launch_plan_device(const PlanDev& h, const int32_t* ctx, int32_t* meta, void* stream);
+int launch_gather_ceiling(Params p, uint32_t* sink, void* stream);
 bool mfma_supported(const Params& p);
 // Host checks of a uniform split call other than its partial buffers
 // (descriptor, arguments, split count, grid limits, kernel family).

@@ -170,40 +170,6 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int first, int nv, in
 
 }  // namespace
 
-// Wait until at most n vector-memory operations of this wave are outstanding.
-// Direct-to-LDS loads count in vmcnt; the compiler does not order later LDS
-// reads after them, so every stage is consumed after an explicit wait.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
-}
-
-// One direct-to-LDS load per lane (16 or 4 bytes): lane l's bytes land at
-// lds + l * size. Issued as inline assembly so that the compiler neither
-// reorders LDS reads around it nor adds its own (draining) waits; every
-// consumer waits with wait_vm.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-}
-// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-}
-
-// Page-table entry read through the constant address space: the table is
-// read-only for the whole call, so uniform reads become scalar loads.
-__device__ __forceinline__ int cload(const int* p) {
-  return *(const __attribute__((address_space(4))) int*)p;
-}
-
 template <class QT, class KT, int D, int NRH, bool VT, bool TM>
 __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int EB = Storage<KT>::bytes;
@@ -853,29 +819,11 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         s[v] = vis ? s[v] : -INFINITY;
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    // ---- lazy rescale: the reference only rises when a logit exceeds it by
-    // more than 2^8 (rare; the wave votes first)
-    const bool need = (mrun == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
-    if (__any(need)) {
-      pin_acc();
-      const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
-      const float mnew = fmaxf(mrun, mt + mu);
-      const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
-      const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
-      lrun *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] -= shift;
-      mrun = mnew;
-      pin_acc();
-    }
-    // ---- probabilities times the V scale as the bf16 P^T operand
+    // ---- probabilities against the current reference. The reference only
+    // rises when a probability would exceed 2^8 (a logit more than 2^8 above
+    // it), which a lane's sum above 2^8 reveals without a row maximum (rare:
+    // the wave votes first; rows without a reference yet always take that
+    // path, which sets it from the row maximum and recomputes the block)
     bf16x8 pf[2];
     {
       float lsum = 0.0f;
@@ -884,6 +832,30 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       for (int v = 0; v < 16; ++v) {
         pe[v] = fexp2(s[v]);
         lsum += pe[v];
+      }
+      const bool need = (mrun == -INFINITY) || !(lsum <= kRescaleLimit);
+      if (__any(need)) {
+        pin_acc();
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+        const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
+        const float mnew = fmaxf(mrun, mt + mu);
+        const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
+        const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
+        lrun *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+        lsum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          pe[v] = fexp2(s[v] - shift);
+          lsum += pe[v];
+        }
+        mrun = mnew;
+        pin_acc();
       }
       lrun += lsum;
       if constexpr (QUANT) {

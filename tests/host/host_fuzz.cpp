@@ -21,6 +21,7 @@ int launch_partial_valu(Params, void*) { ++g_launches; return SKV_OK; }
 int launch_partial_mfma(Params, void*) { ++g_launches; return SKV_OK; }
 int launch_combine(Params, void*) { ++g_launches; return SKV_OK; }
 int launch_plan_device(const PlanDev&, const int32_t*, int32_t*, void*) { ++g_launches; return SKV_OK; }
+int launch_gather_ceiling(Params, uint32_t*, void*) { ++g_launches; return SKV_OK; }
 bool mfma_supported(const Params& p) { return p.q_dtype == SKV_BF16 && p.block_size >= 16; }
 }  // namespace skv
 

@@ -421,3 +421,17 @@ def test_host_plan_call_checks_size_and_header_before_launching():
                                                      ctypes.byref(p), None) == -8
     assert L.skv_attention_decode_paged_planned_host(ctypes.byref(d), ctypes.byref(a), None, cap,
                                                      ctypes.byref(p), None) == -1
+
+
+def test_gather_ceiling_checks_arguments_before_launching():
+    """skv_gather_ceiling (measurement only) validates like the partial stage:
+    a NULL sink, a short sink and unsupported layouts fail before any launch."""
+    L = _lib()
+    fake = 1 << 20
+    a = skv.Args(fake, fake, fake, fake, fake, fake, fake, None, fake, None)
+    d = _desc(B=2, R=4, Hq=16, Hkv=1, D=128)
+    assert L.skv_gather_ceiling(ctypes.byref(d), ctypes.byref(a), 4, None, None, 8, None) == -1
+    assert L.skv_gather_ceiling(ctypes.byref(d), ctypes.byref(a), 4, None, fake, 7, None) == -5   # 2*4*1 > 7
+    assert L.skv_gather_ceiling(ctypes.byref(d), ctypes.byref(a), 0, None, fake, 8, None) == -4
+    small = _desc(B=2, R=4, Hq=16, Hkv=1, D=128, bs=8)
+    assert L.skv_gather_ceiling(ctypes.byref(small), ctypes.byref(a), 4, None, fake, 8, None) == -6

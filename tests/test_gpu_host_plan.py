@@ -66,3 +66,21 @@ def test_host_plan_full_size_bitwise(n, over):
     del p
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_gather_ceiling_runs_on_the_bench_layouts():
+    """The measurement gather (skv_gather_ceiling) over a reduced B200-shaped
+    problem in each layout bench.py --ceiling uses: it completes, writes one
+    value per workgroup, and the same inputs give the same values."""
+    for over in ({}, {"block_size": 128}, {"v_layout": "transposed"}, {"block_size": 128, "v_layout": "transposed"}):
+        p = make_problem(small_spec(4, **over), seed=90, device="cuda")
+        d, a, _ = desc_args(p)
+        s = p.spec
+        hints = skv.plan_hints_for(d, True, partitions_per_request=s.partitions_per_request)
+        plan = skv.Plan(hints, list(s.ctx), p.device)
+        sink = torch.full((plan.capacity * s.Hkv,), -1, dtype=torch.int32, device="cuda")
+        skv.gather_ceiling(d, a, plan.capacity, sink, plan_meta_dev=plan.dev)
+        first = sink.clone()
+        skv.gather_ceiling(d, a, plan.capacity, sink, plan_meta_dev=plan.dev)
+        torch.cuda.synchronize()
+        assert torch.equal(first, sink), over
