@@ -308,6 +308,23 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   }
   ilo = __builtin_amdgcn_readfirstlane(ilo);
   ihi = __builtin_amdgcn_readfirstlane(ihi);
+  // 8-bit score paths: this thread's 32 query elements (one row, one 32-d
+  // block), loaded before the first blocks' page-table reads
+  u32x4 qpre[4] = {};
+  if constexpr (__is_same(KT, FP8) || __is_same(KT, I8)) {
+    if constexpr (__is_same(QT, BF16)) {
+      static_assert(32 * NRH * (D / 32) <= 256 * NRH, "one query block per thread");
+      const int row = tid / (D / 32), blk = tid - row * (D / 32);
+      const int r = rbase + row;
+      if (row < 32 * NRH && r < p.rho) {
+        int j, hq;
+        row_jh(p, g, r, &j, &hq);
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qpre[u] = ld16(src + 8 * u);
+      }
+    }
+  }
 
   floatx16 acc[DB];
   float mrun = -INFINITY, lrun = 0.0f;
@@ -500,13 +517,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         float x[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) x[i] = 0.0f;
-        if (r < p.rho) {
-          int j, hq;
-          row_jh(p, g, r, &j, &hq);
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
+        {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const u32x4 w = ld16(src + 8 * u);
+            const u32x4 w = qpre[u];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
@@ -560,13 +574,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         float x[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) x[i] = 0.0f;
-        if (r < p.rho) {
-          int j, hq;
-          row_jh(p, g, r, &j, &hq);
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + qo_idx(p, b, j, hq, 32 * blk);
+        {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const u32x4 w = ld16(src + 8 * u);
+            const u32x4 w = qpre[u];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[8 * u + 2 * e] = __uint_as_float(w[e] << 16);
