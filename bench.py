@@ -441,16 +441,22 @@ def table(args) -> int:
 # same step on a full-size workload and set against the same workload's
 # default call: (row, config, spec overrides, record dtype, step mode).
 NEXT_ROWS = [
-    ("B200x200k fp8 MTP4 (default call)", 4, {}, "f32", "two_stage"),
-    ("fp16 Q/O", 4, {"q_dtype": "f16"}, "f32", "two_stage"),
-    ("bf16 partial records", 4, {}, "bf16", "two_stage"),
+    ("B200x200k fp8 MTP4 (default call)", 4, {}, "f32", "auto"),
+    ("fp16 Q/O", 4, {"q_dtype": "f16"}, "f32", "auto"),
+    ("bf16 partial records", 4, {}, "bf16", "auto"),
     ("single-kernel split + merge", 4, {}, "f32", "fused"),
     ("device-side plan refresh", 4, {}, "f32", "device_plan"),
-    ("MTP4 rows under a random tree mask", 4, {"verify": "tree"}, "f32", "two_stage"),
-    ("int8 verifier R16 (default call)", 3, {}, "f32", "two_stage"),
-    ("int8 verifier, random tree mask", 3, {"verify": "tree"}, "f32", "two_stage"),
-    ("int8 verifier, independent-batch mask", 3, {"verify": "independent"}, "f32", "two_stage"),
-    ("int8 verifier, fp16 Q/O", 3, {"q_dtype": "f16"}, "f32", "two_stage"),
+    ("MTP4 rows under a random tree mask", 4, {"verify": "tree"}, "f32", "auto"),
+    ("int8 verifier R16 (default call)", 3, {}, "f32", "auto"),
+    ("int8 verifier, two-stage call with the plan copied to the device", 3, {}, "f32", "two_stage"),
+    ("int8 verifier, single-kernel split + merge", 3, {}, "f32", "fused"),
+    ("int8 verifier, device-side plan refresh", 3, {}, "f32", "device_plan"),
+    ("int8 verifier, random tree mask", 3, {"verify": "tree"}, "f32", "auto"),
+    ("int8 verifier, independent-batch mask", 3, {"verify": "independent"}, "f32", "auto"),
+    ("int8 verifier, fp16 Q/O", 3, {"q_dtype": "f16"}, "f32", "auto"),
+    ("mixed batch one 200000 + fifteen 1024 (default call)", 5, {}, "f32", "auto"),
+    ("mixed batch, single-kernel split + merge", 5, {}, "f32", "fused"),
+    ("mixed batch, device-side plan refresh", 5, {}, "f32", "device_plan"),
 ]
 
 
@@ -475,7 +481,9 @@ def next_rows(args) -> int:
                "partial_us_mean": round(part_us, 2),
                "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
                "partial_roofline_frac": round(alg / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-               "steps": steps, "warmup": warmup}
+               "step_mode": r["mode"], "steps": steps, "warmup": warmup}
+        if r["mode"] == "host_plan":
+            row["note"] = "partial_us_mean is the whole planned call (partial + combine)"
         if mode == "fused":
             row["note"] = "partial_us_mean is the fused kernel (split + merge)"
         if n not in base:
