@@ -26,7 +26,9 @@
 //    a stream one issues the K and scale loads, the other the V loads. With
 //    four stages and plain V one workgroup barrier per two blocks publishes
 //    them and frees the two stages refilled meanwhile; otherwise one barrier
-//    per block, with NS - 1 blocks in flight.
+//    per block, with NS - 1 blocks in flight. With one row half a stream is
+//    one wave that loads everything it reads: its own load counter is the
+//    only wait, and the key loop has no barrier.
 //  * Per block a wave reads from LDS only its K operand rows, V (issued
 //    before the softmax, whose vector work hides the read latency) and one K
 //    and one V scale per lane; DPP row broadcasts hand each lane the scales
@@ -666,26 +668,43 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   // all masking; on the others (a wave-uniform test) small branches mask
   // logits, V scales and V codes. The matrix-core code is shared by both
   // kinds, so the accumulators keep one register assignment.
-  auto compute = [&](int t0, int st, auto&& mid) __attribute__((always_inline)) {
+  //
+  // A block runs in five pieces: the K operand reads (kread), S^T = K Q^T
+  // (scores), the V operand reads, scales and logits (prep), the
+  // probabilities and their sum (expsum), and the rescale and
+  // O^T += V^T P^T (finish).
+  constexpr int NKR = F8QK ? 2 * KS8 : (I8QK ? KSI : NCH);
+  struct KOp {
+    u32x4 r[NKR];
+  };
+  auto kread = [&](int st) __attribute__((always_inline)) {
     const char* S = ring + st * STAGE;
-    const bool boundary =
-        __builtin_amdgcn_readfirstlane((int)((t0 + 32 > hi) | (t0 < ilo) | (t0 + 32 > ihi) | (TM && t0 + 32 > dbase))) != 0;
-    const int kb = 16 * hh;                       // first key of this lane's 16
-    // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
-    floatx16 s;
+    KOp k;
     if constexpr (F8QK) {
-      u32x4 ka[KS8][2];
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int c = 4 * ks + hh + 2 * u;       // 16-byte chunk of the key row
-          ka[ks][u] = *reinterpret_cast<const u32x4*>(S + krow + ((c ^ kswz(tau(i32))) * 16));
+          k.r[2 * ks + u] = *reinterpret_cast<const u32x4*>(S + krow + ((c ^ kswz(tau(i32))) * 16));
         }
+    } else if constexpr (I8QK) {
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) k.r[ks] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ ks) * 16));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) k.r[c] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
+    }
+    return k;
+  };
+  // ---- S^T = K Q^T (the first k-step starts from an inline zero accumulator)
+  auto scores = [&](const KOp& k) __attribute__((always_inline)) {
+    floatx16 s;
+    if constexpr (F8QK) {
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks) {
-        const i32x8 a = __builtin_bit_cast(i32x8, u32x8{ka[ks][0][0], ka[ks][0][1], ka[ks][0][2], ka[ks][0][3],
-                                                            ka[ks][1][0], ka[ks][1][1], ka[ks][1][2], ka[ks][1][3]});
+        const u32x4 k0 = k.r[2 * ks], k1 = k.r[2 * ks + 1];
+        const i32x8 a = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
         const i32x8 bh = __builtin_bit_cast(i32x8, u32x8{qa[ks][0][0], qa[ks][0][1], qa[ks][0][2], qa[ks][0][3],
                                                              qa[ks][1][0], qa[ks][1][1], qa[ks][1][2], qa[ks][1][3]});
         const i32x8 bl = __builtin_bit_cast(i32x8, u32x8{qb[ks][0][0], qb[ks][0][1], qb[ks][0][2], qb[ks][0][3],
@@ -695,13 +714,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       }
     } else if constexpr (I8QK) {
       // int8 codes straight from LDS; S = (S_hi << 7) + S_lo is exact (|S| < 2^30)
-      u32x4 kc[KSI];
-#pragma unroll
-      for (int ks = 0; ks < KSI; ++ks) kc[ks] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ ks) * 16));
       i32x16 sh, sl;
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) {
-        const v4i32 a = __builtin_bit_cast(v4i32, kc[ks]);
+        const v4i32 a = __builtin_bit_cast(v4i32, k.r[ks]);
         sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qih[ks]), ks == 0 ? i32x16{} : sh,
                                                    0, 0, 0);
         sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qil[ks]), ks == 0 ? i32x16{} : sl,
@@ -710,33 +726,41 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = (float)((sh[v] << 7) + sl[v]);
     } else {
-    // all operand reads first, so that their latency overlaps instead of
-    // stalling each product
-    u32x4 kc[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kc[c] = *reinterpret_cast<const u32x4*>(S + krow + ((kx ^ c) * 16));
+      for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int h2 = 0; h2 < KPC; ++h2) {
-        const int kk = c * KPC + h2;
-        qop kf;
-        if constexpr (__is_same(QT, F16)) {
-          kf = cvt8h<KT>(kc[c][2 * h2], kc[c][2 * h2 + 1]);
-        } else if constexpr (EB == 1) {
-          kf = cvt8<KT>(kc[c][2 * h2], kc[c][2 * h2 + 1], 0u, 0u);
-        } else {
-          kf = cvt8<KT>(kc[c][0], kc[c][1], kc[c][2], kc[c][3]);
+        for (int h2 = 0; h2 < KPC; ++h2) {
+          const int kk = c * KPC + h2;
+          qop kf;
+          if constexpr (__is_same(QT, F16)) {
+            kf = cvt8h<KT>(k.r[c][2 * h2], k.r[c][2 * h2 + 1]);
+          } else if constexpr (EB == 1) {
+            kf = cvt8<KT>(k.r[c][2 * h2], k.r[c][2 * h2 + 1], 0u, 0u);
+          } else {
+            kf = cvt8<KT>(k.r[c][0], k.r[c][1], k.r[c][2], k.r[c][3]);
+          }
+          s = mfma(kf, qf[kk], kk == 0 ? floatx16{} : s);
         }
-        s = mfma(kf, qf[kk], kk == 0 ? floatx16{} : s);
       }
     }
-    }
-    mid();                                        // e.g. the next block's loads
+    return s;
+  };
+  struct Blk {
+    floatx16 t;                                   // logits t = s * c - mu (masked: -inf)
+    float pe[16];                                 // probabilities exp2(t) (expsum)
+    float lsum, xv, mu;
+    int nv;                                       // keys of this lane's 16 inside the split
+    bool boundary;
+    uint32_t xr[DB][8];                           // V^T operand words
+  };
+  auto prep = [&](int t0, int st, const floatx16& s, Blk& B) __attribute__((always_inline)) {
+    const char* S = ring + st * STAGE;
+    B.boundary =
+        __builtin_amdgcn_readfirstlane((int)((t0 + 32 > hi) | (t0 < ilo) | (t0 + 32 > ihi) | (TM && t0 + 32 > dbase))) != 0;
+    const int kb = 16 * hh;                       // first key of this lane's 16
     // ---- V^T operand reads, ahead of the softmax that hides their latency:
     // xr[db] holds d-block db (transposed V: EB 16-byte key runs; plain V: per
     // key half kh, words 4 kh + [0, 4))
-    uint32_t xr[DB][8];
     if constexpr (VT) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -744,7 +768,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         for (int e = 0; e < EB; ++e) {
           const u32x4 vc = *reinterpret_cast<const u32x4*>(S + KSZ + hh * U * 512 + (db * EB + e) * 512 + i32 * 16);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xr[db][4 * e + q] = vc[q];
+          for (int q = 0; q < 4; ++q) B.xr[db][4 * e + q] = vc[q];
         }
     } else {
       // transposing LDS reads: in each 16-lane group (wave half hh, d half mh
@@ -764,9 +788,9 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
             const char* a8 = vg + key * RB + ((c ^ vswz(key)) * 16) + 8 * (gi & 1);
             const v2i32 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) v2i32*)(a8));
-            xr[db][4 * kh] = (uint32_t)t[0];
-            xr[db][4 * kh + 1] = (uint32_t)t[1];
-            xr[db][4 * kh + 2] = xr[db][4 * kh + 3] = 0u;
+            B.xr[db][4 * kh] = (uint32_t)t[0];
+            B.xr[db][4 * kh + 1] = (uint32_t)t[1];
+            B.xr[db][4 * kh + 2] = B.xr[db][4 * kh + 3] = 0u;
           } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -776,8 +800,8 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
               const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (__attribute__((address_space(3))) v4i16*)(a16));
               const u32x2 u = __builtin_bit_cast(u32x2, t);
-              xr[db][4 * kh + 2 * q] = u[0];
-              xr[db][4 * kh + 2 * q + 1] = u[1];
+              B.xr[db][4 * kh + 2 * q] = u[0];
+              B.xr[db][4 * kh + 2 * q + 1] = u[1];
             }
           }
         }
@@ -787,18 +811,18 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     // lane l reads the scales of key kb + l % 16 only; row broadcasts hand
     // each lane those of its 16 keys
     float c[16];
-    float xv = 1.0f;
-    const int nv = hi - (t0 + kb);                // keys of this lane's 16 inside the split
+    B.xv = 1.0f;
+    B.nv = hi - (t0 + kb);
     if constexpr (QUANT) {
       const float* sc = reinterpret_cast<const float*>(S + KSZ + VSZ);
       const float xk = sc[kb + (lane & 15)] * p.scale_log2;
-      xv = sc[32 + kb + (lane & 15)];
-      if (boundary) {
+      B.xv = sc[32 + kb + (lane & 15)];
+      if (B.boundary) {
         // the V scales of keys past the split may be NaN: zero them, so masked
         // keys give exactly zero (the empty asm keeps this a branch)
-        int n = nv;
+        int n = B.nv;
         asm volatile("" : "+v"(n));
-        xv = ((lane & 15) < n) ? xv : 0.0f;
+        B.xv = ((lane & 15) < n) ? B.xv : 0.0f;
       }
       if constexpr (I8QK) {
         // the query row's scale 2^(e - 7) rides on the broadcast (v_mul_f32_dpp)
@@ -817,43 +841,50 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     // ---- logits t = s * c - mu (mu: the running reference maximum), so that
     // the probability is exp2(t); boundary blocks then replace masked logits
     // by -inf with selects (never by multiplying with zero)
-    const float mu = (mrun == -INFINITY) ? 0.0f : mrun;
+    B.mu = (mrun == -INFINITY) ? 0.0f : mrun;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = __builtin_fmaf(s[v], c[v], -mu);
-    if (boundary) {
+    for (int v = 0; v < 16; ++v) B.t[v] = __builtin_fmaf(s[v], c[v], -B.mu);
+    if (B.boundary) {
       asm volatile("");
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int k = t0 + kb + v;
         bool vis = (k < hi) & (k >= vlo) & (k < vhi);
         if constexpr (TM) vis &= tree_visible(tmask, k, dbase);
-        s[v] = vis ? s[v] : -INFINITY;
+        B.t[v] = vis ? B.t[v] : -INFINITY;
       }
     }
-    // ---- probabilities against the current reference. The reference only
-    // rises when a probability would exceed 2^8 (a logit more than 2^8 above
-    // it), which a lane's sum above 2^8 reveals without a row maximum (rare:
-    // the wave votes first; rows without a reference yet always take that
-    // path, which sets it from the row maximum and recomputes the block)
+  };
+  // ---- probabilities against the current reference
+  auto expsum = [&](Blk& B) __attribute__((always_inline)) {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      B.pe[v] = fexp2(B.t[v]);
+      lsum += B.pe[v];
+    }
+    B.lsum = lsum;
+  };
+  auto finish = [&](Blk& B) __attribute__((always_inline)) {
+    // The reference only rises when a probability would exceed 2^8 (a logit
+    // more than 2^8 above it), which a lane's sum above 2^8 reveals without a
+    // row maximum (rare: the wave votes first; rows without a reference yet
+    // always take that path, which sets it from the row maximum and
+    // recomputes the block)
     bf16x8 pf[2];
     {
-      float lsum = 0.0f;
-      float pe[16], pv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pe[v] = fexp2(s[v]);
-        lsum += pe[v];
-      }
+      float lsum = B.lsum;
+      float pv[16];
       const bool need = (mrun == -INFINITY) || !(lsum <= kRescaleLimit);
       if (__any(need)) {
         pin_acc();
         float mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, B.t[v]);
         const float mt = fmaxf(mx, __shfl_xor(mx, 32, 64));   // row max - mu
-        const float mnew = fmaxf(mrun, mt + mu);
+        const float mnew = fmaxf(mrun, mt + B.mu);
         const float alpha = (mnew == -INFINITY) ? 1.0f : fexp2(mrun - mnew);   // 0 when mrun = -inf
-        const float shift = (mnew == -INFINITY) ? 0.0f : mnew - mu;
+        const float shift = (mnew == -INFINITY) ? 0.0f : mnew - B.mu;
         lrun *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -862,19 +893,19 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         lsum = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          pe[v] = fexp2(s[v] - shift);
-          lsum += pe[v];
+          B.pe[v] = fexp2(B.t[v] - shift);
+          lsum += B.pe[v];
         }
         mrun = mnew;
         pin_acc();
       }
       lrun += lsum;
       if constexpr (QUANT) {
-        row_bcast_mul8<0>(xv, pe, pv);
-        row_bcast_mul8<8>(xv, pe, pv);
+        row_bcast_mul8<0>(B.xv, B.pe, pv);
+        row_bcast_mul8<8>(B.xv, B.pe, pv);
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pv[v] = pe[v];
+        for (int v = 0; v < 16; ++v) pv[v] = B.pe[v];
       }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -885,19 +916,21 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     }
     // ---- O^T += V^T P^T (V codes of keys past the split zeroed on boundary
     // blocks: they may be NaN-poisoned)
-    if (boundary) {
+    if (B.boundary) {
       asm volatile("");
+      const int nv = B.nv;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         if constexpr (VT) {
 #pragma unroll
-          for (int q = 0; q < 4 * EB; ++q) xr[db][q] = keep_bytes(xr[db][q], q * (4 / EB), nv, 4 / EB);
+          for (int q = 0; q < 4 * EB; ++q) B.xr[db][q] = keep_bytes(B.xr[db][q], q * (4 / EB), nv, 4 / EB);
         } else {
           constexpr int PW = 4 / EB;               // keys per word
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int q = 0; q < 2 * EB; ++q) xr[db][4 * kh + q] = keep_bytes(xr[db][4 * kh + q], 8 * kh + q * PW, nv, PW);
+            for (int q = 0; q < 2 * EB; ++q)
+              B.xr[db][4 * kh + q] = keep_bytes(B.xr[db][4 * kh + q], 8 * kh + q * PW, nv, PW);
         }
       }
     }
@@ -907,15 +940,23 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       for (int kh = 0; kh < 2; ++kh) {
         bf16x8 vf;
         if constexpr (VT && EB == 1) {
-          vf = cvt8<KT>(xr[db][2 * kh], xr[db][2 * kh + 1], 0u, 0u);
+          vf = cvt8<KT>(B.xr[db][2 * kh], B.xr[db][2 * kh + 1], 0u, 0u);
         } else {
-          vf = cvt8<KT>(xr[db][4 * kh], xr[db][4 * kh + 1], xr[db][4 * kh + 2], xr[db][4 * kh + 3]);
+          vf = cvt8<KT>(B.xr[db][4 * kh], B.xr[db][4 * kh + 1], B.xr[db][4 * kh + 2], B.xr[db][4 * kh + 3]);
         }
         acc[db] = mfma(vf, pf[kh], acc[db]);
       }
     // The accumulators only meet VALU code in the rare rescale and at the
     // end: keep them in one register assignment across blocks.
     pin_acc();
+  };
+  auto compute = [&](int t0, int st, auto&& mid) __attribute__((always_inline)) {
+    const floatx16 s = scores(kread(st));
+    mid();                                        // e.g. the next block's loads
+    Blk B;
+    prep(t0, st, s, B);
+    expsum(B);
+    finish(B);
   };
 
   // ---- the key loop ----------------------------------------------------------
@@ -946,7 +987,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
     stage_q();
     for (int j = 0; j < steps; j += 2) {
       wait_vm<0>();                               // blocks j, j + 1: everything this wave issued
-      __syncthreads();
+      if constexpr (NRH != 1) __syncthreads();
       auto loads0 = [&]() __attribute__((always_inline)) {
         if (j + 2 < mine) issue(t0_of(j + 2), ids0, (j + 2) % NS);
       };
@@ -978,7 +1019,9 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
         const int r = mine - 1 - j;               // own blocks issued after block j: min(r, NS - 2)
         wait_own(r < NS - 2 ? r : NS - 2);
       }
-      __syncthreads();
+      // With one row half every wave reads only the blocks it loads itself,
+      // so its own wait suffices; two row halves share each stream's blocks.
+      if constexpr (NRH != 1) __syncthreads();
       const int jn = j + NS - 1;
       auto next_loads = [&]() __attribute__((always_inline)) {
         if (jn < mine) issue(t0_of(jn), ids, jn % NS);
