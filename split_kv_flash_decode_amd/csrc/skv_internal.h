@@ -39,7 +39,6 @@ struct Params {
   int32_t finalize;      // 1: single pass, write o instead of a partial record
   int32_t n_items;       // work items in the grid
   int32_t row_groups;    // row groups per (item, KV head)
-  int32_t item_base;     // first work item of this launch
   int32_t q_dtype, kv_dtype, v_layout, block_size, impl;
   int32_t rec_bf16;      // 1: record acc in bf16
   // A plan passed by value (skv_attention_decode_paged_planned_host): the

@@ -10,10 +10,7 @@
 // FP32 scales, page sizes 16 and 128, plain and transposed V).
 //
 // gfx950 design
-//  * One workgroup per (work item, KV head, group of up to 64 query rows);
-//    an eight-wave launch whose last round would leave half of the CUs idle
-//    runs that round's items as a second, four-wave launch with two groups
-//    of 32 rows per item.
+//  * One workgroup per (work item, KV head, group of up to 64 query rows).
 //    Every query row of a KV head (R * Hq / Hkv rows: GQA heads times MTP or
 //    verify rows) shares each key and value loaded, so a block of 32 keys is a
 //    dense contraction: S^T = K Q^T and O^T += V^T P^T run on
@@ -272,7 +269,7 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   const int rg = blk % p.row_groups;
   blk /= p.row_groups;
   const int g = blk % p.Hkv;
-  const int item = p.item_base + blk / p.Hkv;
+  const int item = blk / p.Hkv;
   Item it;
   if (!decode_item(p, item, &it)) return;
   const int b = it.b;
@@ -1172,8 +1169,14 @@ bool mfma_supported(const Params& p) {
   return p.kv_cap % 16 == 0 && mfma_offsets_fit(0, p.v_layout, p.D, p.kv_cap, eb);
 }
 
-// The dtype dispatch of one launch with nrh row halves per workgroup.
-int launch_partial_mfma_split(const Params& p, int nrh, void* stream, int64_t grid) {
+int launch_partial_mfma(Params p, void* stream) {
+  // two row halves (eight waves, two per SIMD) when a KV head has more than
+  // 32 query rows; D = 256 keeps one (its accumulators need the registers)
+  const int rows = mfma_group_rows(p.D, p.rho);
+  const int nrh = rows / 32;
+  p.row_groups = (p.rho + rows - 1) / rows;
+  const int64_t grid = (int64_t)p.n_items * p.Hkv * p.row_groups;
+  if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
   if (p.q_dtype == SKV_F16) {
     switch (p.kv_dtype) {
       case SKV_INT8: return launch_d<F16, I8>(p, nrh, stream, grid);
@@ -1187,45 +1190,6 @@ int launch_partial_mfma_split(const Params& p, int nrh, void* stream, int64_t gr
     case SKV_FP8_E4M3: return launch_d<BF16, FP8>(p, nrh, stream, grid);
   }
   return SKV_ERR_DTYPE;
-}
-
-int launch_partial_mfma(Params p, void* stream) {
-  // two row halves (eight waves, two per SIMD) when a KV head has more than
-  // 32 query rows; D = 256 keeps one (its accumulators need the registers)
-  const int rows = mfma_group_rows(p.D, p.rho);
-  int nrh = rows / 32;
-  p.row_groups = (p.rho + rows - 1) / rows;
-  int64_t grid = (int64_t)p.n_items * p.Hkv * p.row_groups;
-  if (grid > 0x7FFFFFFF) return SKV_ERR_SHAPE;
-  // A launch of eight-wave workgroups (one per CU) whose last round would
-  // fill at most half of the CUs runs that round as a second launch: the
-  // same items with the four-wave kernel and two row groups of 32 rows each,
-  // so every CU works in the tail. The records and outputs are the same bits
-  // (each row's arithmetic is the same in both kernels); the single-kernel
-  // merge, which counts a fixed number of workgroups per request, keeps one
-  // launch.
-  static const int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    return n;
-  }();
-  if (nrh == 2 && p.rho <= 64 && !p.counters && cus > 0 && grid > cus) {
-    const int64_t tail = grid % cus;
-    const int64_t items_b = (tail + p.Hkv - 1) / p.Hkv;
-    if (tail > 0 && 2 * items_b * p.Hkv <= cus && items_b < p.n_items) {
-      Params a = p;
-      a.n_items = p.n_items - (int)items_b;
-      const int rc = launch_partial_mfma_split(a, 2, stream, (int64_t)a.n_items * p.Hkv);
-      if (rc != SKV_OK) return rc;
-      p.item_base = a.n_items;
-      p.n_items = (int)items_b;
-      p.row_groups = 2;
-      nrh = 1;
-      grid = items_b * p.Hkv * 2;
-    }
-  }
-  return launch_partial_mfma_split(p, nrh, stream, grid);
 }
 
 }  // namespace skv
