@@ -32,8 +32,10 @@
 //  * Per block a wave reads from LDS only its K operand rows, V (issued
 //    before the softmax, whose vector work hides the read latency) and one K
 //    and one V scale per lane; DPP row broadcasts hand each lane the scales
-//    of its 16 keys. Q (fp8 parts or bf16) stays in registers for the whole
-//    key loop, and the accumulators stay in arch VGPRs.
+//    of its 16 keys. Q (fp8 or int8 parts, or bf16) stays in registers for
+//    the whole key loop (the int8 parts at D 256 are re-read from LDS per
+//    block), and the accumulators stay in arch VGPRs (AGPRs with one row
+//    half).
 //  * Key order inside a 32-key block is permuted (tau) so that the S^T output
 //    a lane holds is 16 consecutive keys of one query row: exactly the P^T
 //    operand of the P.V product. Plain-layout V reaches the V^T operand through
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   constexpr int KS8 = D / 64;
   int qsh[KS8], qsl[KS8];
   const int q8off = (32 * rh + i32) * QS8 + 16 * hh;
-  // Q stays in registers for the whole key loop (fp8 parts, or bf16).
+  // Q stays in registers for the whole key loop (fp8 parts, or bf16; the
+  // int8 parts too, except at D 256).
   u32x4 qa[KS8][2], qb[KS8][2];
   constexpr int KPC = 16 / (8 * EB);              // k-steps per 16-byte chunk
   constexpr int KS = NCH * KPC;                   // k-steps of 16 d
@@ -639,8 +642,10 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       const int qrow = (32 * rh + i32) * QS8 + hh * (D / 2);
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) {
-        qih[ks] = *reinterpret_cast<const u32x4*>(&qh_s[qrow + 16 * ks]);
-        qil[ks] = *reinterpret_cast<const u32x4*>(&ql_s[qrow + 16 * ks]);
+        if constexpr (D != 256) {
+          qih[ks] = *reinterpret_cast<const u32x4*>(&qh_s[qrow + 16 * ks]);
+          qil[ks] = *reinterpret_cast<const u32x4*>(&ql_s[qrow + 16 * ks]);
+        }
       }
       qrs = qr_s[32 * rh + i32];
     } else if constexpr (!F8QK) {
@@ -718,9 +723,20 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) {
         const v4i32 a = __builtin_bit_cast(v4i32, k.r[ks]);
-        sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qih[ks]), ks == 0 ? i32x16{} : sh,
+        // at D 256 the two parts are read from LDS per k-step: held in
+        // registers they push the kernel past its arch VGPRs, and the
+        // compiler then serializes the K operand reads
+        u32x4 qh, ql;
+        if constexpr (D == 256) {
+          qh = *reinterpret_cast<const u32x4*>(&qh_s[(32 * rh + i32) * QS8 + hh * (D / 2) + 16 * ks]);
+          ql = *reinterpret_cast<const u32x4*>(&ql_s[(32 * rh + i32) * QS8 + hh * (D / 2) + 16 * ks]);
+        } else {
+          qh = qih[ks];
+          ql = qil[ks];
+        }
+        sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qh), ks == 0 ? i32x16{} : sh,
                                                    0, 0, 0);
-        sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, qil[ks]), ks == 0 ? i32x16{} : sl,
+        sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, __builtin_bit_cast(v4i32, ql), ks == 0 ? i32x16{} : sl,
                                                    0, 0, 0);
       }
 #pragma unroll
