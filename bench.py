@@ -274,42 +274,14 @@ PAGE_TABLE = [
 ]
 
 
-def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f32",
-                mode: str = "two_stage", event_free_pass: bool = False, excl_plan_pass: bool = False,
-                problem=None) -> dict:
-    """Generate the workload (or take ``problem``), run the planned step (host
-    plan refresh, metadata copy, partial, combine) ``warmup`` + ``steps`` times.
-
-    ``mode`` "two_stage": host plan refresh, metadata copy, partial, combine;
-    "host_plan": host plan refresh, then the planned call with the plan block
-    passed to the kernels by value (no copy; its event time is reported as
-    the partial time, combine 0); "auto": host_plan when the plan block fits
-    the kernels' argument block, else two_stage; "fused": the single-kernel
-    split + merge instead of partial + combine (its time is reported as the
-    partial time, combine 0);
-    "device_plan": the plan refreshed on the GPU from the device lengths
-    instead of on the host. In the timed steps only the partial kernel is
-    bracketed by events (each event record adds a few microseconds to the
-    stream); the combine's time comes from a few extra steps afterwards.
-    ``event_free_pass``: the time per step comes from a first timed pass
-    without any event (on short steps even two records per step are a
-    visible share), the kernel times from a second pass with events; a third
-    pass times each step alone (events around the step) after a 1 GiB buffer
-    write has pushed the inputs out of L2 and the 256 MB last-level cache
-    (``cold_ms``, the median): the cache-cold time of workloads small enough
-    to stay cache-resident between back-to-back steps.
-    ``excl_plan_pass``: one more pass of ``steps`` steps with the plan left as
-    it is (lengths unchanged): partial + combine only (``ms_excl_plan``).
-    Returns a dict: ms (per step), part_ms, comb_ms (lists), plan, problem,
-    cold_ms, ms_excl_plan (None when not measured)."""
+def make_step(spec, p, record_dtype: str = "f32", mode: str = "two_stage"):
+    """The planned step of ``timed_steps`` on problem ``p``: returns
+    (step(ev=None, refresh=True), plan, output tensor, resolved mode)."""
     import torch
 
     import split_kv_flash_decode_amd as skv
-    from skvgen import make_problem
 
-    dev = torch.device("cuda:0")
-    p = problem if problem is not None else make_problem(spec, seed=seed, device=dev)
-    torch.cuda.synchronize()
+    dev = p.q.device
     o = torch.empty_like(p.q)
     d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
                       window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks,
@@ -357,6 +329,47 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
             skv.splitkv_combine(d, a, plan.capacity, ws, plan_meta_dev=plan.dev)
         if ev is not None and len(ev) > 2:
             ev[2].record(stream)
+
+    return step, plan, o, mode
+
+
+def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f32",
+                mode: str = "two_stage", event_free_pass: bool = False, excl_plan_pass: bool = False,
+                problem=None) -> dict:
+    """Generate the workload (or take ``problem``), run the planned step (host
+    plan refresh, metadata copy, partial, combine) ``warmup`` + ``steps`` times.
+
+    ``mode`` "two_stage": host plan refresh, metadata copy, partial, combine;
+    "host_plan": host plan refresh, then the planned call with the plan block
+    passed to the kernels by value (no copy; its event time is reported as
+    the partial time, combine 0); "auto": host_plan when the plan block fits
+    the kernels' argument block, else two_stage; "fused": the single-kernel
+    split + merge instead of partial + combine (its time is reported as the
+    partial time, combine 0);
+    "device_plan": the plan refreshed on the GPU from the device lengths
+    instead of on the host. In the timed steps only the partial kernel is
+    bracketed by events (each event record adds a few microseconds to the
+    stream); the combine's time comes from a few extra steps afterwards.
+    ``event_free_pass``: the time per step comes from a first timed pass
+    without any event (on short steps even two records per step are a
+    visible share), the kernel times from a second pass with events; a third
+    pass times each step alone (events around the step) after a 1 GiB buffer
+    write has pushed the inputs out of L2 and the 256 MB last-level cache
+    (``cold_ms``, the median): the cache-cold time of workloads small enough
+    to stay cache-resident between back-to-back steps.
+    ``excl_plan_pass``: one more pass of ``steps`` steps with the plan left as
+    it is (lengths unchanged): partial + combine only (``ms_excl_plan``).
+    Returns a dict: ms (per step), part_ms, comb_ms (lists), plan, problem,
+    cold_ms, ms_excl_plan (None when not measured)."""
+    import torch
+
+    from skvgen import make_problem
+
+    dev = torch.device("cuda:0")
+    p = problem if problem is not None else make_problem(spec, seed=seed, device=dev)
+    torch.cuda.synchronize()
+    step, plan, o, mode = make_step(spec, p, record_dtype, mode)
+    stream = torch.cuda.current_stream()
 
     for _ in range(warmup):
         step()
@@ -410,6 +423,41 @@ def timed_steps(spec, seed: int, steps: int, warmup: int, record_dtype: str = "f
             "output": o, "mode": mode}
 
 
+def rotated_step_ms(spec, seed: int, mode: str = "auto", sets: int = 3, iters: int = 101, runs: int = 3) -> float:
+    """The timing method of the planned-reduction page's Performance setup:
+    ``sets`` independently allocated copies of the workload (their own inputs,
+    plans and workspaces), rotated from one iteration to the next so that
+    consecutive steps do not find each other's data in the caches; ``runs``
+    runs of ``iters`` iterations, each timed as a whole with HIP events; the
+    median of the runs' mean step times (ms)."""
+    import statistics
+
+    import torch
+
+    from skvgen import make_problem
+
+    dev = torch.device("cuda:0")
+    probs = [make_problem(spec, seed=seed + 1000 * k, device=dev) for k in range(sets)]
+    steps = [make_step(spec, p, "f32", mode)[0] for p in probs]
+    torch.cuda.synchronize()
+    for k in range(2 * sets):                        # warm-up of every set
+        steps[k % sets]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    res = []
+    for _ in range(runs):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(iters):
+            steps[k % sets]()
+        e1.record(stream)
+        e1.synchronize()
+        res.append(e0.elapsed_time(e1) / iters)
+    del probs, steps
+    torch.cuda.empty_cache()
+    return statistics.median(res)
+
+
 def table(args) -> int:
     import torch
 
@@ -422,18 +470,23 @@ def table(args) -> int:
         r = timed_steps(spec, n, steps, warmup, event_free_pass=True, mode="auto")
         ms, part_ms, comb_ms, plan, p, cold_ms = r["ms"], r["part_ms"], r["comb_ms"], r["plan"], r["problem"], r["cold_ms"]
         tbs = spec_bytes(spec) / (ms * 1e-3) / 1e12
+        step_mode, items = r["mode"], plan.info.num_items
+        del p, r, plan
+        torch.cuda.empty_cache()
+        rot_ms = rotated_step_ms(spec, n)
         print(json.dumps({"row": f"{name}, page {bs}, {vl} V", "us_per_step": round(ms * 1e3, 2),
                           "effective_TBps": round(tbs, 3),
                           "us_per_step_cache_cold": round(cold_ms * 1e3, 2),
                           "effective_TBps_cache_cold": round(spec_bytes(spec) / (cold_ms * 1e-3) / 1e12, 3),
+                          "us_per_step_page_method": round(rot_ms * 1e3, 2),
+                          "effective_TBps_page_method": round(spec_bytes(spec) / (rot_ms * 1e-3) / 1e12, 3),
                           "page_us_per_step": page_us,
                           "page_TBps": page_tbs, "time_vs_page": round(ms * 1e3 / page_us, 4),
+                          "time_vs_page_page_method": round(rot_ms * 1e3 / page_us, 4),
                           "partial_us_mean": round(sum(part_ms) / len(part_ms) * 1e3, 2),
                           "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
-                          "plan_items": plan.info.num_items, "step_mode": r["mode"],
+                          "plan_items": items, "step_mode": step_mode,
                           "steps": steps, "warmup": warmup}), flush=True)
-        del p
-        torch.cuda.empty_cache()
     return 0
 
 
@@ -668,7 +721,8 @@ def main(argv=None) -> int:
                     help="only run 1 GiB device-to-device copies (counter calibration)")
     ap.add_argument("--table", action="store_true",
                     help="time the six rows of the planned-reduction page's Performance table "
-                         "(one JSON line per row, with the page's own time beside ours)")
+                         "(one JSON line per row: back to back, cache-cold, and with the page's own "
+                         "method of three rotated allocation sets; the page's time beside ours)")
     ap.add_argument("--next", action="store_true",
                     help="time the adjacent variants (fp16 Q/O, bf16 records, fused call, device "
                          "plan refresh, verify masks) against the default call on the same workloads")
