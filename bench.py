@@ -508,6 +508,8 @@ NEXT_ROWS = [
     ("int8 verifier, independent-batch mask", 3, {"verify": "independent"}, "f32", "auto"),
     ("int8 verifier, fp16 Q/O", 3, {"q_dtype": "f16"}, "f32", "auto"),
     ("mixed batch one 200000 + fifteen 1024 (default call)", 5, {}, "f32", "auto"),
+    ("mixed batch, the long request at index 9 of 16", 5, {"ctx": (1024,) * 9 + (200000,) + (1024,) * 6}, "f32",
+     "auto"),
     ("mixed batch, single-kernel split + merge", 5, {}, "f32", "fused"),
     ("mixed batch, device-side plan refresh", 5, {}, "f32", "device_plan"),
 ]

@@ -14,8 +14,9 @@ output, both kernel families. So do the adjacent variants ``bench.py --next``
 times (fp16 Q/O, bf16 records, verify masks, the device plan refresh), in
 that same step, on the same samples; bf16 records add the bound of their own
 rounding (2^-8 times the oracle's output on |V|). The other three B200 rows
-of the planned-reduction page's Performance table (page 128, transposed V)
-and the mixed batch with a 4096-key window and sinks run here as well.
+of the planned-reduction page's Performance table (page 128, transposed V),
+the mixed batch with a 4096-key window and sinks, and the mixed batch with
+its long request in the middle of the batch run here as well.
 """
 
 from __future__ import annotations
@@ -36,6 +37,15 @@ pytestmark = pytest.mark.gpu
 SAMPLES = {2: None, 3: None, 4: (0, 97, 199), 5: (0, 1, 15)}
 
 
+def _samples(n, spec):
+    """Requests checked: SAMPLES, except that the mixed batch always checks
+    its long request (wherever it sits), the one after it and the last."""
+    if n != 5:
+        return SAMPLES[n] or range(spec.B)
+    long_b = max(range(spec.B), key=lambda i: spec.ctx[i])
+    return sorted({long_b, (long_b + 1) % spec.B, spec.B - 1})
+
+
 def _record(name, b, ctx, st):
     """Append one request's error statistics to $SKV_ACCURACY_OUT (JSON lines),
     when that variable names a file: the per-workload accuracy summary."""
@@ -53,7 +63,7 @@ def test_full_size_bench_step_matches_oracle(n):
     p = make_problem(spec, seed=4, device="cuda")
     o, ws, plan = bench_step(p, ws_fill=float("nan"))
     out = to_f64(o)
-    reqs = SAMPLES[n] or range(spec.B)
+    reqs = _samples(n, spec)
     try:
         for b in reqs:
             sub = extract_request(p, b)
@@ -92,6 +102,8 @@ VARIANTS = [
     ("cfg4_bs128_transposed", 4, {"block_size": 128, "v_layout": "transposed"}, "f32", False),
     # the mixed batch with the 4096-key sliding window and per-head sinks
     ("cfg5_window4096_sinks", 5, {"window": 4096, "sinks": True}, "f32", False),
+    # the mixed batch with its long request in the middle of the batch
+    ("cfg5_long_at_9", 5, {"ctx": (1024,) * 9 + (200000,) + (1024,) * 6}, "f32", False),
     # sharp queries (Q x 8, |O| ~ 1): where the 5e-3 relative bound bites at full size
     ("cfg4_sharp", 4, {"q_mult": 8.0}, "f32", False),
     ("cfg3_sharp", 3, {"q_mult": 8.0}, "f32", False),
@@ -116,7 +128,7 @@ def test_full_size_variant_rows_match_oracle(name, n, over, rec, dev_plan):
     assert o.dtype == p.q.dtype
     out = to_f64(o)
     try:
-        for b in SAMPLES[n] or range(spec.B):
+        for b in _samples(n, spec):
             sub = extract_request(p, b)
             extra = 2.0 ** -8 * oracle_abs_value_output(sub)[0] if rec == "bf16" else None
             st = compare(out[b], oracle_output(sub)[0], "lowp", extra=extra)

@@ -82,6 +82,21 @@ def test_planned_with_descriptor_hints_matches_oracle(n):
     _check(p, o, n, f"cfg{n} planned, descriptor hints")
 
 
+@pytest.mark.parametrize("ctx", [(1024, 300, 6000, 1024), (300, 1024, 1024, 6000), (1024, 6000, 0, 300)],
+                         ids=["long_at_2", "long_last", "long_at_1_empty_at_2"])
+def test_mixed_batch_with_the_long_request_elsewhere(ctx):
+    """The mixed batch with its long request moved away from index 0: the
+    planner's work list, slot map and the combine must follow each request,
+    not its position."""
+    p = _problem(5, seed=27, ctx=ctx)
+    for mode in ("planned", "split"):
+        for impl in IMPLS[5]:
+            if mode == "planned" and impl == "valu":
+                continue
+            o, _, _ = run(p, mode, num_splits=5, impl=impl, ws_fill=float("nan"))
+            _check(p, o, 5, f"cfg5 ctx {ctx} {mode} {impl}")
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_sharp_variant(n):
     p = _problem(n, seed=30 + n, q_mult=8.0)
