@@ -553,8 +553,10 @@ def next_rows(args) -> int:
 
 def timed_uniform(spec, S: int, seed: int, steps: int, warmup: int, problem=None) -> dict:
     """The uniform-split call (skv_attention_decode_paged_splitkv with S
-    splits: partial + combine, no plan) timed like ``timed_steps``: a pass
-    without events (warm), then each call alone after a 1 GiB write (cold)."""
+    splits, or skv_attention_decode_splitkv for a problem laid out
+    contiguously: partial + combine, no plan) timed like ``timed_steps``: a
+    pass without events (warm), then each call alone after a 1 GiB write
+    (cold)."""
     import torch
 
     import split_kv_flash_decode_amd as skv
@@ -563,15 +565,16 @@ def timed_uniform(spec, S: int, seed: int, steps: int, warmup: int, problem=None
     dev = torch.device("cuda:0")
     p = problem if problem is not None else make_problem(spec, seed=seed, device=dev)
     o = torch.empty_like(p.q)
-    d = skv.make_desc(p.q, p.k, p.v, paged=True, v_layout=spec.v_layout, causal=spec.causal,
+    d = skv.make_desc(p.q, p.k, p.v, paged=p.paged, v_layout=spec.v_layout, causal=spec.causal,
                       window=spec.window, scale=spec.scale, page_table=p.page_table, has_sink=spec.sinks)
     a = skv.make_args(p.q, p.k, p.v, p.ctx, o, k_scale=p.k_scale, v_scale=p.v_scale,
                       page_table=p.page_table, sinks=p.sinks)
     ws = skv.Workspace(d, skv.uniform_slots(d, S), dev)
     stream = torch.cuda.current_stream()
+    split_call = skv.attention_decode_paged_splitkv if p.paged else skv.attention_decode_splitkv
 
     def call():
-        skv.attention_decode_paged_splitkv(d, a, S, ws)
+        split_call(d, a, S, ws)
 
     for _ in range(warmup):
         call()
@@ -638,6 +641,25 @@ def all_configs(args) -> int:
                               "frac_warm": round(nbytes / (u["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "frac_cold": round(nbytes / (u["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "steps": steps, "warmup": warmup}), flush=True)
+        if n == 1:
+            # the single request also as a contiguous cache (no page table)
+            from skvgen import to_contiguous
+            c = to_contiguous(p)
+            cbytes = logical_bytes(spec.ctx, R=spec.R, Hq=spec.Hq, Hkv=spec.Hkv, D=spec.D, q_bytes=_DT[spec.q_dtype],
+                                   kv_bytes=_DT[spec.kv_dtype], quantized=spec.kv_dtype in ("int8", "fp8"),
+                                   block_size=spec.block_size, paged=False)
+            for S in (spec.splits or ()):
+                u = timed_uniform(spec, S, n, steps, warmup, problem=c)
+                print(json.dumps({"config": n, "workload": workload_name(spec).replace("page 16, ", "contiguous, "),
+                                  "mode": f"uniform S={S}",
+                                  "us_per_step_warm": round(u["ms"] * 1e3, 2),
+                                  "us_per_step_cold": round(u["cold_ms"] * 1e3, 2),
+                                  "TBps_warm": round(cbytes / (u["ms"] * 1e-3) / 1e12, 4),
+                                  "TBps_cold": round(cbytes / (u["cold_ms"] * 1e-3) / 1e12, 4),
+                                  "frac_warm": round(cbytes / (u["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "frac_cold": round(cbytes / (u["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "steps": steps, "warmup": warmup}), flush=True)
+            del c
         del r, p
         torch.cuda.empty_cache()
     return 0
