@@ -991,9 +991,11 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   if constexpr (NS >= 4 && !VT) {
     // Two blocks per barrier: it publishes blocks j, j + 1 and frees the
     // stages of j - 2, j - 1, into which j + 2 and j + 3 are loaded while j
-    // and j + 1 are computed (their loads go out between the two matrix-core
-    // phases of each block, so the waves do not all queue on the vector
-    // memory unit at once). Page ids are read one barrier step ahead.
+    // and j + 1 are computed. The loads of j + 2 go out between the two
+    // matrix-core phases of block j and those of j + 3 between the two
+    // blocks, so both are in flight through block j + 1's whole step and the
+    // waves do not all queue on the vector memory unit at once. Page ids are
+    // read one barrier step ahead.
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       if (j < mine) issue(t0_of(j), load_ids(t0_of(j)), j);
@@ -1010,14 +1012,13 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
       auto loads1 = [&]() __attribute__((always_inline)) {
         if (j + 3 < mine) issue(t0_of(j + 3), ids1, (j + 3) % NS);
       };
+      auto none = []() __attribute__((always_inline)) {};
       if (j < mine)
         compute(t0_of(j), j % NS, loads0);
       else
         loads0();
-      if (j + 1 < mine)
-        compute(t0_of(j + 1), (j + 1) % NS, loads1);
-      else
-        loads1();
+      loads1();
+      if (j + 1 < mine) compute(t0_of(j + 1), (j + 1) % NS, none);
       if (j + 4 < mine) ids0 = load_ids(t0_of(j + 4));
       if (j + 5 < mine) ids1 = load_ids(t0_of(j + 5));
     }
