@@ -34,6 +34,8 @@ SKV_IMPL_AUTO, SKV_IMPL_VALU, SKV_IMPL_MFMA = 0, 1, 2
 SKV_SPLIT_ALIGN = 64
 SKV_MAX_SPLITS = 256
 SKV_PLAN_INLINE_MAX = 480
+(SKV_OK, SKV_ERR_NULL, SKV_ERR_SHAPE, SKV_ERR_DTYPE, SKV_ERR_SPLITS, SKV_ERR_CAPACITY, SKV_ERR_UNSUPPORTED,
+ SKV_ERR_LAUNCH, SKV_ERR_PLAN, SKV_ERR_ALIGN, SKV_ERR_SCRATCH) = range(0, -11, -1)
 
 _c_i32 = ctypes.c_int32
 _c_ptr = ctypes.c_void_p

@@ -36,6 +36,19 @@ def test_library_exports_every_declared_function():
     assert skv.abi_version() == 4
 
 
+def test_binding_constants_match_the_header():
+    with open(os.path.join(ROOT, "include", "skv.h")) as f:
+        text = f.read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"^#define (SKV_\w+) \(?(-?\d+)\)?", text, re.M)}
+    codes = [n for n in defs if n == "SKV_OK" or n.startswith("SKV_ERR_")]
+    assert len(codes) >= 11, codes
+    for n in codes + ["SKV_MAX_SPLITS", "SKV_SPLIT_ALIGN"]:
+        assert getattr(skv, n) == defs[n], n
+    for n in codes:
+        if n != "SKV_OK":
+            assert skv.status_str(defs[n]) != "unknown status", n
+
+
 def _desc(**kw):
     _lib()
     q = torch.zeros(kw.pop("B", 2), kw.pop("R", 4), kw.pop("Hq", 16), kw.pop("D", 128),
