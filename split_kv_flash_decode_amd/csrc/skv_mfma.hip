@@ -24,9 +24,9 @@
 //  * K, V and the per-token scales go from HBM straight into a per-stream LDS
 //    ring (global_load_lds of whole key rows, NS stages). Of the two waves of
 //    a stream one issues the K and scale loads, the other the V loads. With
-//    four stages and plain V one workgroup barrier per two blocks publishes
-//    them and frees the two stages refilled meanwhile; otherwise one barrier
-//    per block, with NS - 1 blocks in flight. With one row half a stream is
+//    four stages one workgroup barrier per two blocks publishes them and
+//    frees the two stages refilled meanwhile; otherwise one barrier per
+//    block, with NS - 1 blocks in flight. With one row half a stream is
 //    one wave that loads everything it reads: its own load counter is the
 //    only wait, and the key loop has no barrier.
 //  * Per block a wave reads from LDS only its K operand rows, V (issued
@@ -984,11 +984,9 @@ __global__ __launch_bounds__(256 * NRH) void partial_mfma(Params p) {
   const int mine = nblk > sid ? (nblk - 1 - sid) / 4 + 1 : 0;
   const int steps = (nblk + 3) / 4;
   auto t0_of = [&](int j) __attribute__((always_inline)) { return lo + (sid + 4 * j) * 32; };
-  // Two blocks per barrier for plain V with four stages; one block per
-  // barrier (NS - 1 blocks in flight instead of two) for transposed V and
-  // fewer stages, where the deeper prefetch measured faster than the saved
-  // barriers.
-  if constexpr (NS >= 4 && !VT) {
+  // Two blocks per barrier with four stages; one block per barrier when the
+  // ring holds fewer (D 256, 16-bit codes at D 128).
+  if constexpr (NS >= 4) {
     // Two blocks per barrier: it publishes blocks j, j + 1 and frees the
     // stages of j - 2, j - 1, into which j + 2 and j + 3 are loaded while j
     // and j + 1 are computed. The loads of j + 2 go out between the two
