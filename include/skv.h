@@ -439,9 +439,11 @@ int skv_splitkv_fused(const skv_desc* d, const skv_args* a, int32_t paged, int32
  * [PA] Performance, bandwidth note), with the matrix-core partial kernel's
  * memory pattern: one workgroup per (work item, KV head), four key streams of
  * 32-key blocks, page-table reads per 16-key group, 16-byte-per-lane
- * direct-to-LDS loads of whole rows, the same ring depth, waits and
- * barriers, and no arithmetic. Its time is the floor those loads put under
- * the partial kernel. Work items as skv_splitkv_partial (plan_meta NULL:
+ * direct-to-LDS loads of whole rows, the same ring depth, one workgroup
+ * barrier per block with all but one stage in flight (the faster of the
+ * partial kernel's two load schedules when nothing is computed), and no
+ * arithmetic. Its time is the floor those loads put under the partial
+ * kernel. Work items as skv_splitkv_partial (plan_meta NULL:
  * uniform num_splits; else the device plan block, num_splits = its C).
  * sink: DEVICE uint32 [sink_len] >= items * Hkv (one value per workgroup,
  * overwritten). Paged calls with block_size >= 16 and 8-bit codes, or bf16

@@ -9,9 +9,11 @@
 // head), four key streams taking interleaved 32-key blocks of the item's
 // split range), its page-table reads (scalar loads of the page ids of a
 // block's two 16-key groups), its 16-byte-per-lane direct-to-LDS loads of
-// whole K rows, V rows (or V^T runs) and one dword of scales per lane, its
-// ring depth and its per-block waits and barriers, and does no arithmetic on
-// the data. Its time per launch is the floor the partial kernel's loads put
+// whole K rows, V rows (or V^T runs) and one dword of scales per lane and its
+// ring depth, and does no arithmetic on the data. It waits and synchronizes
+// once per block with all but one stage in flight: of the partial kernel's
+// two schedules (that one, and one barrier per two blocks after a full wait)
+// the faster for a loop that computes nothing. Its time per launch is the floor the partial kernel's loads put
 // under it; the partial kernel's own time over this one is the share of the
 // memory ceiling it reaches.
 
