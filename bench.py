@@ -8,7 +8,12 @@ refreshes the plan from host-known context lengths and copies its metadata to
 the device, then the partial kernel and the combine kernel run (the timed
 step of aiter #5628 "tune MTP work budgets and planned reduction",
 Performance: plan refresh, attention and reduction on every call). Inputs are
-resident in HBM before timing starts. Prints one JSON line:
+resident in HBM before timing starts. After W warm-up steps, K steps are
+timed as a whole with no event on the stream (value, ms_per_step); a second
+pass of K steps brackets each partial launch with HIP events (roofline), then
+ten more steps the combine, K more with the plan left unchanged, and up to 50
+steps each timed alone after a 1 GiB write has evicted the caches. Prints one
+JSON line:
 
   value       effective TB/s = logical bytes / time per step, where logical
               bytes count Q and O, the valid K and V codes and their scales,
@@ -802,9 +807,9 @@ def main(argv=None) -> int:
     spec = config_spec(args.config, **overrides)
     print(f"[bench] generating {spec.name} on cuda:0 and timing ...", file=sys.stderr, flush=True)
     t = time.time()
-    r = timed_steps(spec, args.seed, args.steps, args.warmup, excl_plan_pass=True)
+    r = timed_steps(spec, args.seed, args.steps, args.warmup, event_free_pass=True, excl_plan_pass=True)
     ms_per_step, part_ms, comb_ms, plan = r["ms"], r["part_ms"], r["comb_ms"], r["plan"]
-    ms_excl_plan = r["ms_excl_plan"]
+    ms_excl_plan, ms_cold = r["ms_excl_plan"], r["cold_ms"]
     print(f"[bench] done in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     del r
     nbytes = spec_bytes(spec)
@@ -829,6 +834,7 @@ def main(argv=None) -> int:
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "us_per_step_excl_plan": round(ms_excl_plan * 1e3, 2),
+        "us_per_step_cache_cold": round(ms_cold * 1e3, 2),
         "hbm_fraction": round(tbs * 1e3 / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -850,9 +856,13 @@ def main(argv=None) -> int:
             "plan_capacity": plan.capacity,
             "partial_us_mean": round(part_mean * 1e3, 2),
             "combine_us_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 2),
-            "timing": ("value and ms_per_step: wall clock over the timed steps, each a host plan "
-                       "refresh + metadata copy + partial + combine; us_per_step_excl_plan: the same "
-                       "number of steps with the plan left unchanged (partial + combine only)"),
+            "timing": ("value and ms_per_step: wall clock over the timed steps (no event on the "
+                       "stream), each a host plan refresh + metadata copy + partial + combine; kernel "
+                       "times: HIP events around each partial launch in a second pass of as many "
+                       "steps (and around the combine in ten more); us_per_step_excl_plan: the same "
+                       "number of steps with the plan left unchanged (partial + combine only); "
+                       "us_per_step_cache_cold: median of steps timed alone, each after a 1 GiB "
+                       "write evicts L2 and the last-level cache"),
         },
         "roofline": {
             "bound": "hbm",
