@@ -13,9 +13,9 @@
 // ring depth, and does no arithmetic on the data. It waits and synchronizes
 // once per block with all but one stage in flight: of the partial kernel's
 // two schedules (that one, and one barrier per two blocks after a full wait)
-// the faster for a loop that computes nothing. Its time per launch is the floor the partial kernel's loads put
-// under it; the partial kernel's own time over this one is the share of the
-// memory ceiling it reaches.
+// the faster for a loop that computes nothing. Its time per launch is the
+// floor the partial kernel's loads put under it; the partial kernel's own
+// time over this one is the share of the memory ceiling it reaches.
 
 #include "skv_device.h"
 
