@@ -29,7 +29,7 @@ import pytest
 import torch
 
 from skvgen import config_spec, extract_request, make_problem
-from tests.gpu_run import bench_step, to_f64
+from tests.gpu_run import bench_step, run, to_f64
 from tests.helpers import compare, oracle_abs_value_output, oracle_output
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +74,36 @@ def test_full_size_bench_step_matches_oracle(n):
             assert st["ok"], (n, b, st)
     finally:
         del p, o, ws, plan
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_full_size_run_to_run_bitwise(n):
+    """At full size, the single-pass call (num_splits = 1) and the planned
+    step each give the same bits twice in a row, and the planned step's whole
+    output matches the single pass within the workload tolerance (any split
+    count equals the single pass)."""
+    spec = config_spec(n)
+    p = make_problem(spec, seed=5, device="cuda")
+    try:
+        a, _, _ = run(p, "single")
+        a = a.clone()
+        b, _, _ = run(p, "single")
+        same = torch.equal(a, b)
+        print(f"[full cfg{n}] single pass twice: bitwise {same}", flush=True)
+        assert same, n
+        s1, _, _ = bench_step(p, ws_fill=float("nan"))
+        s1 = s1.clone()
+        s2, _, _ = bench_step(p, ws_fill=float("nan"))
+        same = torch.equal(s1, s2)
+        print(f"[full cfg{n}] planned step twice: bitwise {same}", flush=True)
+        assert same, n
+        st = compare(to_f64(s1), to_f64(a), "lowp")
+        print(f"[full cfg{n}] planned step vs single pass: {st}", flush=True)
+        assert st["ok"], (n, st)
+    finally:
+        del p
         gc.collect()
         torch.cuda.empty_cache()
 
